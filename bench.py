@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark: grouped-query attention decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one ``gqa_decode`` call over the whole batch (split kernel + merge
+kernel), i.e. one layer's attention for one decode step.  Inputs are seeded
+synthetic tensors already resident in HBM; before every timed step a 1 GiB
+read sweeps the L2 and the Infinity Cache so that K/V come from HBM.
+
+Useful bytes per step (the algorithmic traffic; "GQA (Grouped-Query
+Attention) 분석", section "KV cache 용량", per layer and step):
+    2 * sum_b(L_b) * G * D * s_kv   (K and V rows each read once)
+  + |Q| + |O|                        (query in, fp32 output out)
+The n_rep-times repeated K/V of a repeat_kv path is NOT counted.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import gqa_inputs as gi  # noqa: E402
+
+METRIC = "GQA decode attention µs/step + achieved KV-read HBM GB/s (% of peak)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+FLUSH_BYTES = 1 << 30
+KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_decode_amd", "csrc", f)
+                  for f in ("gqa_kernels.hip", "gqa_api.cpp", "gqa_internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Accounting
+# ---------------------------------------------------------------------------
+def kv_elem_bytes(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+def useful_bytes(B, H, G, D, sq, sum_len, dtype: str) -> int:
+    s = kv_elem_bytes(dtype)
+    kv = 2 * sum_len * G * D * s
+    q = B * H * sq * D * s
+    o = B * H * sq * D * 4
+    return kv + q + o
+
+
+def flops(H, D, sq, sum_len) -> int:
+    """2 FLOP per multiply-add; scores and weighted sum each H*sq*L*D MACs
+    ("질의 헤드는 그대로, 키·값 헤드만 줄인다", section on what shrinks: the
+    attention body's multiply count has no g term)."""
+    return 4 * H * sq * sum_len * D
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, sha: str):
+    """HBM bytes per split launch from committed rocprofv3 counter runs, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_split_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host cores
+# ---------------------------------------------------------------------------
+def cpu_baseline(x_cpu, w, sum_len, seconds: float):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    q = x_cpu["q"].double().numpy()
+    k = x_cpu["k"].double().numpy()
+    v = x_cpu["v"].double().numpy()
+    sl = x_cpu["seq_lens"].numpy().astype(np.int32)
+    scale = 1.0 / math.sqrt(w.D)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_f64(q, k, v, sl, scale, threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 200:
+            break
+    per = el / passes
+    ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
+    return {"value": ub / per / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (%d sequences), %d passes in %.1f s, float64, "
+                      "%d threads; %.1f ms per pass" % (w.B, passes, el, threads, per * 1e3)}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=gi.HEADLINE, choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cache sweep (warm-cache numbers; not HBM rates)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py runs on exactly one GPU (WORLD_SIZE=%s)" % os.environ["WORLD_SIZE"],
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import grouped_query_attention_decode_amd as gqa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    gqa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = gi.WORKLOADS[args.workload]
+    log("[bench] workload %s: drawing inputs on the GPU" % w.name)
+    x = gi.make_inputs(w, device=dev)
+    sum_len = int(x["seq_lens"].clamp(0, w.T).sum().item())
+    ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
+    path = {"auto": gqa.PATH_AUTO, "valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA}[args.path]
+    shape = gqa.shape_of(x["q"], x["k"])
+    plan = gqa.plan(shape, path=path, chunk_tokens=args.chunk_tokens)
+    log("[bench] plan %s" % plan)
+    out = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(ev_split=None):
+        gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
+                   chunk_tokens=args.chunk_tokens, stream=stream, split_done_event=ev_split)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.sum()
+        call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for trio in ev:                       # create the HIP event handles
+        for e in trio:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    log("[bench] timing %d steps" % K)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        if not args.no_flush:
+            flush.sum()
+        ev[i][0].record(stream)
+        call(ev[i][1])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    split_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms = statistics.fmean(step_ms)
+    q = statistics.quantiles(step_ms, n=10) if K >= 10 else [min(step_ms)] * 9
+    split_avg = statistics.fmean(split_ms)
+
+    # warm-cache reference (labelled; never reported as an HBM rate)
+    warm = []
+    for i in range(min(K, 20)):
+        ev[i][0].record(stream)
+        call()
+        ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        warm.append(ev[i][0].elapsed_time(ev[i][2]))
+
+    # parity spot check of this very run against the oracle (one sequence)
+    parity = None
+    try:
+        import numpy as np
+        import oracle
+        b = 0
+        xb = {k: v[b:b + 1].cpu() for k, v in x.items()}
+        want = oracle.decode_f64(xb["q"], xb["k"], xb["v"], xb["seq_lens"],
+                                 1.0 / math.sqrt(w.D), threads=8)
+        parity = float(np.abs(out[b:b + 1].double().cpu().numpy() - want).max())
+    except Exception as e:  # noqa: BLE001
+        log("[bench] parity spot check skipped: %s" % e)
+
+    gbs = ub / (ms * 1e-3) / 1e9
+    achieved = ub / (split_avg * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    traffic = load_traffic(w.name, sha)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "G": w.G, "D": w.D, "T": w.T,
+            "sq": w.sq, "seq_lens": ("uniform [%d, %d], seed %d" % (w.ragged[0], w.ragged[1], w.seed)
+                                     if w.ragged else "all T"),
+            "sum_seq_lens": sum_len, "kv_dtype": w.dtype, "out_dtype": "f32",
+            "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
+            "path": {1: "valu", 2: "mfma"}.get(plan["path"], "?"),
+            "chunk_tokens": plan["chunk_tokens"],
+        },
+        "us_per_step": round(ms * 1e3, 2),
+        "us_p10": round(q[0] * 1e3, 2),
+        "us_p50": round(statistics.median(step_ms) * 1e3, 2),
+        "us_p90": round(q[8] * 1e3, 2),
+        "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
+        "useful_bytes": ub,
+        "flops": flops(w.H, w.D, w.sq, sum_len),
+        "split_us": round(split_avg * 1e3, 2),
+        "merge_us": round(statistics.fmean(merge_ms) * 1e3, 2),
+        "warm_cache_us_per_step": round(statistics.median(warm) * 1e3, 2),
+        "wall_ms_per_step_incl_sweep": round(wall / K * 1e3, 4),
+        "max_abs_err_vs_oracle_b0": parity,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_valu" if plan["path"] == 1 else "split_mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": (None if traffic is None else traffic["hbm_bytes_per_launch"]),
+            "algorithmic_bytes_per_launch": ub,
+        },
+        "cpu_baseline": None,
+    }
+    if traffic is not None:
+        result["roofline"]["traffic_over_algorithmic"] = round(
+            traffic["hbm_bytes_per_launch"] / ub, 3)
+    if not args.no_cpu:
+        log("[bench] timing the float64 oracle on the host (~%.0f s)" % args.cpu_seconds)
+        del flush
+        xc = {k: v.cpu() for k, v in x.items()}
+        result["cpu_baseline"] = cpu_baseline(xc, w, sum_len, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

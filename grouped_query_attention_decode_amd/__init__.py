@@ -1,0 +1,219 @@
+"""Python binding of libgqa: grouped-query attention at decode time on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libgqa.so`` (built by ``grouped_query_attention_decode_amd.build``);
+torch supplies device memory and the current stream.  If the library is
+missing or fails to load, every call raises -- there is no fallback.
+
+    out = decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None)
+
+q [B,H,sq,D], k_cache / v_cache [B,G,T,D] (contiguous, on one GPU, both
+float32 or both bfloat16), seq_lens [B] int32 on the same GPU or None,
+out [B,H,sq,D] float32.  Query head h reads KV head h // (H/G)
+("GQA (Grouped-Query Attention) 분석", section "Grouped broadcast").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = ["decode", "plan", "workspace_bytes", "version", "library_path",
+           "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
+           "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa.so")
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
+GQA_F32, GQA_BF16 = 0, 1
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+
+# Every symbol include/gqa.h declares.
+EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",
+                    "gqa_decode_ex", "gqa_plan", "gqa_last_error", "gqa_version")
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("libgqa status %d: %s" % (status, message))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("sq", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("split_done_event", ctypes.c_void_p),
+                ("reserved", ctypes.c_int32 * 4)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("max_chunks", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
+                ("row_blocks", ctypes.c_int32), ("split_grid", ctypes.c_int32),
+                ("combine_grid", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libgqa.so (after torch, so that both share one HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgqa.so is not built (%s); run "
+                "`python -m grouped_query_attention_decode_amd.build` "
+                "or __graft_entry__.build()" % LIB_PATH)
+        import torch  # noqa: F401  (loads torch's HIP runtime first)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sp = ctypes.c_void_p, ctypes.POINTER(Shape)
+        i32p = ctypes.c_void_p
+        lib.gqa_decode.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp]
+        lib.gqa_decode.restype = ctypes.c_int
+        lib.gqa_workspace_bytes.argtypes = [sp]
+        lib.gqa_workspace_bytes.restype = ctypes.c_size_t
+        lib.gqa_decode_ws.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
+                                      ctypes.c_size_t, vp]
+        lib.gqa_decode_ws.restype = ctypes.c_int
+        lib.gqa_decode_ex.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
+                                      ctypes.c_size_t, ctypes.POINTER(Options), vp]
+        lib.gqa_decode_ex.restype = ctypes.c_int
+        lib.gqa_plan.argtypes = [sp, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
+        lib.gqa_plan.restype = ctypes.c_int
+        lib.gqa_last_error.argtypes = []
+        lib.gqa_last_error.restype = ctypes.c_char_p
+        lib.gqa_version.argtypes = []
+        lib.gqa_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != GQA_OK:
+        msg = load_library().gqa_last_error().decode(errors="replace")
+        raise GqaError(status, msg)
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float32:
+        return GQA_F32
+    if dt == torch.bfloat16:
+        return GQA_BF16
+    return 99  # rejected by the library as unsupported
+
+
+def make_shape(B, H, G, sq, T, D, q_dtype=GQA_BF16, kv_dtype=GQA_BF16, out_dtype=GQA_F32):
+    return Shape(B, H, G, sq, T, D, q_dtype, kv_dtype, out_dtype)
+
+
+def _options(path=PATH_AUTO, chunk_tokens=0, split_done_event=None):
+    o = Options()
+    o.path = int(path)
+    o.chunk_tokens = int(chunk_tokens)
+    if split_done_event is not None:
+        # a torch.cuda.Event: its hipEvent_t handle (created on first use)
+        o.split_done_event = ctypes.c_void_p(split_done_event.cuda_event)
+    return o
+
+
+def plan(shape: Shape, path=PATH_AUTO, chunk_tokens=0) -> dict:
+    """The planner's launch decisions for ``shape`` (host only)."""
+    lib = load_library()
+    info = PlanInfo()
+    opts = _options(path, chunk_tokens)
+    _check(lib.gqa_plan(ctypes.byref(shape), ctypes.byref(opts), ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(load_library().gqa_workspace_bytes(ctypes.byref(shape)))
+
+
+def version() -> str:
+    return load_library().gqa_version().decode()
+
+
+def shape_of(q, k_cache, out_dtype=None) -> Shape:
+    B, H, sq, D = q.shape
+    _, G, T, _ = k_cache.shape
+    import torch
+    return make_shape(B, H, G, sq, T, D, _dtype_code(q.dtype), _dtype_code(k_cache.dtype),
+                      _dtype_code(out_dtype or torch.float32))
+
+
+def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
+           path=PATH_AUTO, chunk_tokens=0, workspace=None, stream=None,
+           split_done_event=None):
+    """Grouped-query attention for one decode step (see module docstring).
+
+    Runs asynchronously on ``stream`` (default: torch's current stream).
+    ``workspace``: optional uint8 CUDA tensor of at least
+    ``workspace_bytes(shape_of(q, k_cache))`` bytes; default: library-owned.
+    ``split_done_event``: optional torch.cuda.Event (created with
+    ``enable_timing=True`` and already recorded once, so that its handle
+    exists) that the library records between its split and merge kernels.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H,sq,D] and k_cache/v_cache [B,G,T,D]")
+    if q.shape[0] != k_cache.shape[0] or q.shape[3] != k_cache.shape[3]:
+        raise ValueError("q and the caches disagree on B or D")
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a dtype")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    dev = q.device
+    if k_cache.device != dev or v_cache.device != dev:
+        raise ValueError("all tensors must be on one device")
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or seq_lens.device != dev or \
+                seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 [B] tensor on q's device")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    else:
+        if out.shape != q.shape or out.device != dev or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B,H,sq,D] tensor on q's device")
+    D = q.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    shape = shape_of(q, k_cache, out.dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    opts = _options(path, chunk_tokens, split_done_event)
+    ws_ptr, ws_len = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != dev:
+            raise ValueError("workspace must be on q's device")
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.gqa_decode_ex(
+            ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr() if seq_lens is not None else None,
+            ctypes.c_float(scale), out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len),
+            ctypes.byref(opts), sptr)
+    _check(st)
+    return out

@@ -1,0 +1,265 @@
+// gqa_api.cpp -- the C ABI of libgqa (include/gqa.h): argument checks, the
+// chunk planner, the library-owned workspace and the launch.
+//
+// The checks follow the shape rules of "GQA (Grouped-Query Attention) 분석",
+// section "Tensor parallelism과 kernel 제약" (head dims must agree and H must
+// be a multiple of G; the cache is [batch, kv_heads, sequence, head_dim]).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/gqa.h"
+#include "gqa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gqa_status_t fail(gqa_status_t st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gqa_status_t ok()
+{
+    g_last_error[0] = '\0';
+    return GQA_OK;
+}
+
+int pow2_ceil(int x)
+{
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// Validate the shape and options and build the launch plan.
+gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* p)
+{
+    if (!s) return fail(GQA_ERR_INVALID_ARG, "shape is NULL");
+    if (s->B < 0 || s->H <= 0 || s->G <= 0 || s->sq <= 0 || s->T <= 0 || s->D <= 0)
+        return fail(GQA_ERR_INVALID_ARG, "sizes must be positive (B >= 0): B=%d H=%d G=%d sq=%d T=%d D=%d",
+                    s->B, s->H, s->G, s->sq, s->T, s->D);
+    if (s->H % s->G != 0)
+        return fail(GQA_ERR_INVALID_ARG, "H (%d) must be a multiple of G (%d)", s->H, s->G);
+    if (s->D != 64 && s->D != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", s->D);
+    const bool f32 = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32 && s->out_dtype == GQA_F32;
+    const bool bf16 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_BF16 && s->out_dtype == GQA_F32;
+    if (!f32 && !bf16)
+        return fail(GQA_ERR_UNSUPPORTED, "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32) or (BF16,BF16,F32)",
+                    s->q_dtype, s->kv_dtype, s->out_dtype);
+    if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
+        return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
+    const int64_t R64 = (int64_t)(s->H / s->G) * s->sq;
+    if (R64 > (1 << 20)) return fail(GQA_ERR_INVALID_ARG, "(H/G)*sq too large");
+    int path_req = GQA_PATH_AUTO, chunk_req = 0;
+    if (o) {
+        path_req = o->path;
+        chunk_req = o->chunk_tokens;
+        for (int i = 0; i < 4; ++i)
+            if (o->reserved[i] != 0) return fail(GQA_ERR_INVALID_ARG, "options.reserved must be zero");
+        if (path_req < GQA_PATH_AUTO || path_req > GQA_PATH_MFMA)
+            return fail(GQA_ERR_INVALID_ARG, "unknown path %d", path_req);
+        if (chunk_req < 0) return fail(GQA_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
+    }
+    if (path_req == GQA_PATH_MFMA)
+        return fail(GQA_ERR_UNSUPPORTED, "the MFMA path is not built in this version");
+
+    const int R = (int)R64;
+    p->path = gqa::Path::VALU;
+    p->kv_bf16 = bf16 ? 1 : 0;
+    p->D = s->D;
+    p->R = R;
+    p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
+    p->n_rb = (R + p->row_block - 1) / p->row_block;
+
+    // Chunk size: a multiple of the workgroup tile; as large as LDS allows
+    // (scores of chunk * row_block floats <= 32 KB) unless that leaves fewer
+    // than kTargetSplitGroups workgroups, then halved down to one tile.
+    const int tile = gqa::split_tile_rows(p->path, p->kv_bf16, s->D);
+    int ct_max = 8192 / p->row_block;
+    if (ct_max > 2048) ct_max = 2048;
+    ct_max = (ct_max / tile) * tile;
+    if (ct_max < tile) ct_max = tile;
+    const int64_t units = (int64_t)s->B * s->G * p->n_rb;
+    int ct;
+    if (chunk_req > 0) {
+        ct = ((chunk_req + tile - 1) / tile) * tile;
+        if (ct > ct_max) ct = ct_max;
+    } else {
+        ct = tile;
+        while (ct * 2 <= ct_max) ct *= 2;
+        while (ct > tile && units * ((s->T + ct - 1) / ct) < gqa::kTargetSplitGroups) ct /= 2;
+        if (ct % tile) ct = tile;   // keep a whole number of tiles
+    }
+    // one chunk covering the whole cache when the cache is no longer than a tile
+    p->chunk = ct;
+    p->max_chunks = (s->T + ct - 1) / ct;
+    p->split_grid = units * p->max_chunks;
+    if (p->split_grid > 0x7FFFFFFF) return fail(GQA_ERR_INVALID_ARG, "problem too large for one launch");
+    const int64_t rows = (int64_t)s->B * s->H * s->sq;
+    p->combine_grid = p->max_chunks > 1 ? (rows + 3) / 4 : 0;
+    const int lds_main = (ct * p->row_block > gqa::kSplitWaves * p->row_block * s->D)
+                             ? ct * p->row_block
+                             : gqa::kSplitWaves * p->row_block * s->D;
+    p->lds_bytes = (size_t)(lds_main + 2 * p->row_block) * sizeof(float);
+    p->ws_bytes = p->max_chunks > 1 ? (size_t)rows * p->max_chunks * (s->D + 1) * sizeof(float) : 0;
+    return GQA_OK;
+}
+
+struct DeviceWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<DeviceWorkspace> g_ws;
+
+gqa_status_t library_workspace(size_t need, void** out)
+{
+    *out = nullptr;
+    if (need == 0) return GQA_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    DeviceWorkspace& w = g_ws[dev];
+    if (w.bytes < need) {
+        const char* inject = getenv("GQA_TEST_FAIL_ALLOC");
+        if (inject && inject[0] == '1') return fail(GQA_ERR_ALLOC, "workspace allocation failed (injected)");
+        if (w.ptr) {
+            // earlier calls on any stream may still use the old buffer
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t grow = need + need / 4;
+        e = hipMalloc(&w.ptr, grow);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(GQA_ERR_ALLOC, "hipMalloc(%zu) for the workspace: %s", grow, hipGetErrorString(e));
+        }
+        w.bytes = grow;
+    }
+    *out = w.ptr;
+    return GQA_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const void* v,
+                 const int32_t* seq_lens, float scale, void* out, void* workspace, size_t ws_bytes,
+                 bool library_ws, const gqa_options_t* opts, void* stream)
+{
+    gqa::Plan plan;
+    gqa_status_t st = make_plan(shape, opts, &plan);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale must be finite");
+    if (shape->B == 0) return ok();
+    if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+        return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (library_ws) {
+        st = library_workspace(plan.ws_bytes, &workspace);
+        if (st != GQA_OK) return st;
+    } else if (plan.ws_bytes > 0) {
+        if (!workspace || ws_bytes < plan.ws_bytes)
+            return fail(GQA_ERR_ALLOC, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                        workspace ? ws_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+
+    gqa::Args a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.seq_lens = seq_lens;
+    a.out = static_cast<float*>(out);
+    const size_t rows = (size_t)shape->B * shape->H * shape->sq;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = workspace ? a.part_o + rows * plan.max_chunks * shape->D : nullptr;
+    a.B = shape->B;
+    a.H = shape->H;
+    a.G = shape->G;
+    a.sq = shape->sq;
+    a.T = shape->T;
+    a.scale_log2 = scale * 1.4426950408889634f;
+
+    hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream),
+                                      opts ? static_cast<hipEvent_t>(opts->split_done_event) : nullptr);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode(const gqa_shape_t* shape, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                        void* stream)
+{
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, nullptr, 0, true, nullptr, stream);
+}
+
+size_t gqa_workspace_bytes(const gqa_shape_t* shape)
+{
+    gqa::Plan plan;
+    if (make_plan(shape, nullptr, &plan) != GQA_OK) return 0;
+    return plan.ws_bytes;
+}
+
+gqa_status_t gqa_decode_ws(const gqa_shape_t* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                           void* workspace, size_t ws_bytes, void* stream)
+{
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, false, nullptr,
+               stream);
+}
+
+gqa_status_t gqa_decode_ex(const gqa_shape_t* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                           void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
+{
+    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts,
+               stream);
+}
+
+gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_plan_t* plan)
+{
+    if (!plan) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+    gqa::Plan p;
+    gqa_status_t st = make_plan(shape, opts, &p);
+    if (st != GQA_OK) return st;
+    std::memset(plan, 0, sizeof(*plan));
+    plan->path = p.path == gqa::Path::MFMA ? GQA_PATH_MFMA : GQA_PATH_VALU;
+    plan->chunk_tokens = p.chunk;
+    plan->max_chunks = p.max_chunks;
+    plan->rows_per_group = p.R;
+    plan->row_blocks = p.n_rb;
+    plan->split_grid = (int32_t)p.split_grid;
+    plan->combine_grid = (int32_t)p.combine_grid;
+    plan->workspace_bytes = p.ws_bytes;
+    return ok();
+}
+
+const char* gqa_last_error(void) { return g_last_error; }
+
+const char* gqa_version(void) { return "libgqa 0.1.0 (gfx950)"; }
+
+}  // extern "C"

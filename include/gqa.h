@@ -1,0 +1,156 @@
+/*
+ * gqa.h -- C ABI of libgqa: grouped-query attention at decode time on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation ("GQA (Grouped-Query Attention) 분석", sections "Grouped
+ * broadcast" and "동작 원리 / 3. Incremental decode"; "Same GQA, Different
+ * Execution Cost Across Backends", section 1):
+ *
+ *   for every batch row b, query head h, new-token index s:
+ *     g       = h / (H / G)                 (KV head shared by H/G query heads)
+ *     L       = clamp(seq_lens[b], 0, T)    (valid cache rows; T if seq_lens is NULL)
+ *     last    = L - sq + s                  (query s sees cache rows 0..last)
+ *     p       = softmax_j( scale * <q[b,h,s,:], k_cache[b,g,j,:]> ),  j = 0..last
+ *     out[b,h,s,:] = sum_j p_j * v_cache[b,g,j,:]      (zeros when last < 0)
+ *
+ * The sq new tokens are taken to be already appended to the cache, as the
+ * last sq of its L valid rows (the incremental-decode loop on the same
+ * page appends the new K/V before attending).  Each K/V head is read from
+ * device memory once for all H/G query heads that share it; no repeated
+ * copy of K/V is ever made (the cost that "Same GQA, Different Execution
+ * Cost Across Backends", section 2, measures for the repeat_kv path).
+ *
+ * Conventions for every entry point below:
+ *   - Tensor pointers are DEVICE pointers (memory from hipMalloc or any
+ *     allocator of the same device), row-major and contiguous:
+ *       q        [B, H, sq, D]   dtype q_dtype
+ *       k_cache  [B, G, T, D]    dtype kv_dtype
+ *       v_cache  [B, G, T, D]    dtype kv_dtype
+ *       seq_lens [B]             int32, or NULL (every sequence holds T rows)
+ *       out      [B, H, sq, D]   dtype out_dtype
+ *     All must be 16-byte aligned.  out must not overlap the inputs.
+ *   - The caller owns every tensor; the library neither frees nor keeps
+ *     them after the call returns.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous: the work is queued on stream and the call
+ *     returns without waiting; the host never reads seq_lens.
+ *   - Status codes, never an abort.  On a non-OK status nothing was queued
+ *     (GQA_ERR_HIP: a launch failed, and out may be partly written) and
+ *     gqa_last_error() describes the reason.
+ *   - seq_lens values outside [0, T] are clamped on the device.
+ *
+ * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
+ * (F32, F32, F32) or (BF16, BF16, F32); H % G == 0; any B >= 0, sq >= 1,
+ * T >= 1 with T * D < 2^31.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1, /* null pointer, bad sizes, H % G != 0, bad scale   */
+    GQA_ERR_UNSUPPORTED = 2, /* head dim or dtype combination not built          */
+    GQA_ERR_ALLOC = 3,       /* workspace allocation failed or is too small      */
+    GQA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed        */
+} gqa_status_t;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype_t;
+
+/* Problem shape.  H: query heads, G: KV heads ("num_key_value_heads"),
+ * sq: new query tokens per sequence, T: cache capacity in rows, D: head dim. */
+typedef struct {
+    int32_t B, H, G, sq, T, D;
+    int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
+} gqa_shape_t;
+
+/* Kernel choice for the split pass. */
+typedef enum {
+    GQA_PATH_AUTO = 0, /* MFMA when (H/G)*sq >= 16 and inputs are bf16, else VALU */
+    GQA_PATH_VALU = 1, /* vector ALU dot products, any supported shape             */
+    GQA_PATH_MFMA = 2  /* bf16 matrix cores; bf16 inputs only                      */
+} gqa_path_t;
+
+/* Optional knobs; zero-initialise for defaults. */
+typedef struct {
+    int32_t path;            /* gqa_path_t                                             */
+    int32_t chunk_tokens;    /* cache rows per workgroup; 0 = planner's choice.  Rounded
+                                up to the kernel's tile and clamped to its limits.     */
+    void *split_done_event;  /* NULL, or a hipEvent_t the call records on stream right
+                                after queueing the split kernel and before the merge
+                                kernel (lets a caller time the two kernels apart)     */
+    int32_t reserved[4];     /* must be zero                                           */
+} gqa_options_t;
+
+/* What the planner decided for a shape (filled by gqa_plan). */
+typedef struct {
+    int32_t path;           /* GQA_PATH_VALU or GQA_PATH_MFMA                          */
+    int32_t chunk_tokens;   /* cache rows per workgroup                                */
+    int32_t max_chunks;     /* ceil(T / chunk_tokens)                                  */
+    int32_t rows_per_group; /* (H/G)*sq: query rows sharing one KV head                */
+    int32_t row_blocks;     /* workgroups per (b, KV head, chunk) along the rows       */
+    int32_t split_grid;     /* workgroups of the split kernel                          */
+    int32_t combine_grid;   /* workgroups of the merge kernel (0: not launched)        */
+    int32_t reserved;
+    uint64_t workspace_bytes; /* device scratch the call needs                        */
+} gqa_plan_t;
+
+/*
+ * gqa_decode -- out = grouped-query attention (see top of file).
+ * Uses a workspace owned by the library: one buffer per device, grown on
+ * demand (hipMalloc, after waiting for the device) and kept until process
+ * exit.  Calls that run concurrently on different streams of one device
+ * must use gqa_decode_ws with their own workspaces instead.
+ * scale: any finite float (the pages use 1/sqrt(D)).
+ */
+gqa_status_t gqa_decode(const gqa_shape_t *shape, const void *q,
+                        const void *k_cache, const void *v_cache,
+                        const int32_t *seq_lens, float scale, void *out,
+                        void *stream);
+
+/* Device scratch bytes gqa_decode_ws needs for this shape (0 on bad shape). */
+size_t gqa_workspace_bytes(const gqa_shape_t *shape);
+
+/*
+ * gqa_decode_ws -- as gqa_decode, with a caller-owned device workspace of
+ * ws_bytes >= gqa_workspace_bytes(shape) bytes (may be NULL when that is 0).
+ * The workspace must stay untouched until the queued work finishes.
+ */
+gqa_status_t gqa_decode_ws(const gqa_shape_t *shape, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, float scale, void *out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gqa_decode_ex -- as gqa_decode_ws with tuning options (may be NULL).
+ * Results for a given input are deterministic for a given plan; different
+ * chunk sizes agree to rounding.  workspace NULL with ws_bytes 0 selects
+ * the library-owned workspace of gqa_decode.
+ */
+gqa_status_t gqa_decode_ex(const gqa_shape_t *shape, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, float scale, void *out,
+                           void *workspace, size_t ws_bytes,
+                           const gqa_options_t *opts, void *stream);
+
+/* Fill *plan for shape and opts (opts may be NULL).  Host only, no GPU work. */
+gqa_status_t gqa_plan(const gqa_shape_t *shape, const gqa_options_t *opts,
+                      gqa_plan_t *plan);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *gqa_last_error(void);
+
+/* Library version string. */
+const char *gqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

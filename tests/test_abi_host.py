@@ -1,0 +1,150 @@
+"""Host-side checks of libgqa's C ABI: it loads, exports every symbol the
+header declares, plans shapes, and rejects bad arguments before touching a
+GPU.  No kernel is launched.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_attention_decode_amd as gqa
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gqa.library_path()):
+        from grouped_query_attention_decode_amd import build
+        build.build()
+    return gqa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(gqa.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version(lib):
+    assert "gfx950" in gqa.version()
+    assert lib.gqa_last_error() is not None
+
+
+def _shape(**kw):
+    base = dict(B=2, H=32, G=8, sq=1, T=4096, D=128, q_dtype=gqa.GQA_BF16,
+                kv_dtype=gqa.GQA_BF16, out_dtype=gqa.GQA_F32)
+    base.update(kw)
+    return gqa.Shape(**base)
+
+
+def test_plan_of_batched_gqa8(lib):
+    p = gqa.plan(_shape(B=32))
+    assert p["rows_per_group"] == 4
+    assert p["row_blocks"] == 1
+    assert p["max_chunks"] * p["chunk_tokens"] >= 4096
+    assert p["split_grid"] == 32 * 8 * p["max_chunks"]
+    # the workspace holds one (D + 1)-float partial per output row and chunk,
+    # far below a repeated K/V copy (n_rep = 4 times the cache)
+    kv_bytes = 2 * 32 * 8 * 4096 * 128 * 2
+    assert p["workspace_bytes"] == 32 * 32 * p["max_chunks"] * 129 * 4
+    assert p["workspace_bytes"] < kv_bytes // 50
+    assert gqa.workspace_bytes(_shape(B=32)) == p["workspace_bytes"]
+
+
+def test_plan_chunk_option_rounds_to_tile(lib):
+    p = gqa.plan(_shape(), chunk_tokens=100)
+    assert p["chunk_tokens"] % 64 == 0 and p["chunk_tokens"] >= 100
+    p1 = gqa.plan(_shape(T=100), chunk_tokens=0)
+    assert p1["max_chunks"] >= 1
+
+
+def test_plan_row_blocks_for_large_groups(lib):
+    p = gqa.plan(_shape(G=1, sq=2, q_dtype=gqa.GQA_F32, kv_dtype=gqa.GQA_F32), path=gqa.PATH_VALU)
+    assert p["rows_per_group"] == 64
+    assert p["row_blocks"] == 4
+    p = gqa.plan(_shape(H=6, G=1, sq=3), path=gqa.PATH_VALU)
+    assert p["rows_per_group"] == 18 and p["row_blocks"] == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=30, G=8), gqa.GQA_ERR_INVALID_ARG),
+    (dict(G=0), gqa.GQA_ERR_INVALID_ARG),
+    (dict(sq=0), gqa.GQA_ERR_INVALID_ARG),
+    (dict(T=0), gqa.GQA_ERR_INVALID_ARG),
+    (dict(B=-1), gqa.GQA_ERR_INVALID_ARG),
+    (dict(D=96), gqa.GQA_ERR_UNSUPPORTED),
+    (dict(q_dtype=gqa.GQA_F32), gqa.GQA_ERR_UNSUPPORTED),
+    (dict(out_dtype=gqa.GQA_BF16), gqa.GQA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), gqa.GQA_ERR_UNSUPPORTED),
+    (dict(T=1 << 25, D=128), gqa.GQA_ERR_INVALID_ARG),
+])
+def test_bad_shapes_rejected(lib, kw, status):
+    s = _shape(**kw)
+    with pytest.raises(gqa.GqaError) as ei:
+        gqa.plan(s)
+    assert ei.value.status == status
+    assert gqa.workspace_bytes(s) == 0
+    # the decode entry point refuses the same shape before any GPU work
+    st = lib.gqa_decode(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, None)
+    assert st == status
+    assert lib.gqa_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    s = _shape()
+    st = lib.gqa_decode(ctypes.byref(s), None, 16, 16, None, ctypes.c_float(0.1), 16, None)
+    assert st == gqa.GQA_ERR_INVALID_ARG
+    st = lib.gqa_decode(ctypes.byref(s), 18, 16, 16, None, ctypes.c_float(0.1), 16, None)
+    assert st == gqa.GQA_ERR_INVALID_ARG
+    assert "aligned" in lib.gqa_last_error().decode()
+    st = lib.gqa_decode(None, 16, 16, 16, None, ctypes.c_float(0.1), 16, None)
+    assert st == gqa.GQA_ERR_INVALID_ARG
+
+
+def test_non_finite_scale_rejected(lib):
+    s = _shape()
+    for bad in (float("nan"), float("inf")):
+        st = lib.gqa_decode(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(bad), 16, None)
+        assert st == gqa.GQA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    s = _shape(B=0)
+    assert lib.gqa_decode(ctypes.byref(s), None, None, None, None, ctypes.c_float(0.1),
+                          None, None) == gqa.GQA_OK
+    assert lib.gqa_last_error().decode() == ""
+
+
+def test_explicit_workspace_too_small_rejected(lib):
+    s = _shape(B=32)
+    need = gqa.workspace_bytes(s)
+    assert need > 0
+    st = lib.gqa_decode_ws(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16,
+                           16, ctypes.c_size_t(need - 1), None)
+    assert st == gqa.GQA_ERR_ALLOC
+
+
+def test_bad_options_rejected(lib):
+    s = _shape()
+    with pytest.raises(gqa.GqaError) as ei:
+        gqa.plan(s, path=9)
+    assert ei.value.status == gqa.GQA_ERR_INVALID_ARG
+    with pytest.raises(gqa.GqaError):
+        gqa.plan(s, chunk_tokens=-1)
+    o = gqa.Options()
+    o.reserved[2] = 1
+    info = gqa.PlanInfo()
+    assert lib.gqa_plan(ctypes.byref(s), ctypes.byref(o), ctypes.byref(info)) == \
+        gqa.GQA_ERR_INVALID_ARG
