@@ -129,6 +129,9 @@ def main(argv=None):
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 1 GiB device copy (bandwidth reference, "
+                         "and the calibration kernel for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -270,6 +273,22 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
+    if args.copy_probe:
+        src_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(2.0)
+        dst_buf = torch.empty_like(src_buf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(10):
+            flush.sum()
+            e0.record(stream)
+            dst_buf.copy_(src_buf)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        result["copy_probe"] = {"bytes_read": FLUSH_BYTES, "bytes_written": FLUSH_BYTES,
+                                "us": round(statistics.median(times) * 1e3, 2),
+                                "gbs_read_plus_write": round(2 * FLUSH_BYTES / (statistics.median(times) * 1e-3) / 1e9, 1)}
+        del src_buf, dst_buf
     if traffic is not None:
         result["roofline"]["traffic_over_algorithmic"] = round(
             traffic["hbm_bytes_per_launch"] / ub, 3)
