@@ -3,10 +3,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one ``gqa_decode`` call over the whole batch (split kernel + merge
-kernel), i.e. one layer's attention for one decode step.  Inputs are seeded
+One step = one ``gqa_decode`` call over the whole batch (one kernel launch),
+i.e. one layer's attention for one decode step.  Inputs are seeded
 synthetic tensors already resident in HBM; before every timed step a 1 GiB
 read sweeps the L2 and the Infinity Cache so that K/V come from HBM.
+Time per step = (K x [sweep, step] back to back) - (K x [sweep]), over the
+stream, i.e. the kernels' device time; isolated single-call times (which
+also count a lone launch's dispatch latency) are reported beside it.
 
 Useful bytes per step (the algorithmic traffic; "GQA (Grouped-Query
 Attention) 분석", section "KV cache 용량", per layer and step):
@@ -77,7 +80,7 @@ def kernel_source_sha() -> str:
 def load_traffic(workload: str, sha: str):
     """HBM bytes per split launch from committed rocprofv3 counter runs, or
     None when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_split_%s.json" % workload)
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -123,7 +126,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=gi.HEADLINE, choices=sorted(gi.WORKLOADS))
-    ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
@@ -159,15 +162,15 @@ def main(argv=None):
     ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
     path = {"auto": gqa.PATH_AUTO, "valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA}[args.path]
     shape = gqa.shape_of(x["q"], x["k"])
-    plan = gqa.plan(shape, path=path, chunk_tokens=args.chunk_tokens)
+    plan = gqa.plan(shape, path=path, workgroups=args.workgroups)
     log("[bench] plan %s" % plan)
     out = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     stream = torch.cuda.current_stream(dev)
 
-    def call(ev_split=None):
+    def call():
         gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
-                   chunk_tokens=args.chunk_tokens, stream=stream, split_done_event=ev_split)
+                   workgroups=args.workgroups, stream=stream)
 
     for _ in range(args.warmup):
         if not args.no_flush:
@@ -176,39 +179,55 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for trio in ev:                       # create the HIP event handles
-        for e in trio:
-            e.record(stream)
-    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
 
-    log("[bench] timing %d steps" % K)
+    # (1) Each step alone: events right around the decode call.  This also
+    #     counts the dispatch latency of a lone launch (a few us).
+    log("[bench] timing %d isolated steps" % K)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     for i in range(K):
         if not args.no_flush:
             flush.sum()
         ev[i][0].record(stream)
-        call(ev[i][1])
-        ev[i][2].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    iso_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+
+    # (2) The timed region: K steps back to back, each after the cache sweep,
+    #     bracketed by synchronize on both sides; minus the same K sweeps
+    #     alone.  Launches queue behind the sweeps, so dispatch latency is
+    #     hidden as in a decode loop and the difference is the kernels'
+    #     device time -- what rocprofv3 reports per launch.
+    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        if not args.no_flush:
+            flush.sum()
+        call()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
-    split_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    ms = statistics.fmean(step_ms)
+    e2.record(stream)
+    for i in range(K):
+        if not args.no_flush:
+            flush.sum()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    ms = (e0.elapsed_time(e1) - e2.elapsed_time(e3)) / K
+    step_ms = iso_ms
     q = statistics.quantiles(step_ms, n=10) if K >= 10 else [min(step_ms)] * 9
-    split_avg = statistics.fmean(split_ms)
 
     # warm-cache reference (labelled; never reported as an HBM rate)
     warm = []
     for i in range(min(K, 20)):
         ev[i][0].record(stream)
         call()
-        ev[i][2].record(stream)
+        ev[i][1].record(stream)
         torch.cuda.synchronize()
-        warm.append(ev[i][0].elapsed_time(ev[i][2]))
+        warm.append(ev[i][0].elapsed_time(ev[i][1]))
 
     # parity spot check of this very run against the oracle (one sequence)
     parity = None
@@ -224,7 +243,7 @@ def main(argv=None):
         log("[bench] parity spot check skipped: %s" % e)
 
     gbs = ub / (ms * 1e-3) / 1e9
-    achieved = ub / (split_avg * 1e-3) / 1e9
+    achieved = gbs      # one kernel per step: the step is the kernel
     sha = kernel_source_sha()
     traffic = load_traffic(w.name, sha)
     result = {
@@ -247,23 +266,22 @@ def main(argv=None):
             "sum_seq_lens": sum_len, "kv_dtype": w.dtype, "out_dtype": "f32",
             "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
             "path": {1: "valu", 2: "mfma"}.get(plan["path"], "?"),
-            "chunk_tokens": plan["chunk_tokens"],
+            "workgroups": plan["workgroups"],
         },
         "us_per_step": round(ms * 1e3, 2),
-        "us_p10": round(q[0] * 1e3, 2),
-        "us_p50": round(statistics.median(step_ms) * 1e3, 2),
-        "us_p90": round(q[8] * 1e3, 2),
+        "timing": "device time per step: K steps back to back after cache sweeps, minus the sweeps alone",
+        "isolated_call_us_p10": round(q[0] * 1e3, 2),
+        "isolated_call_us_p50": round(statistics.median(step_ms) * 1e3, 2),
+        "isolated_call_us_p90": round(q[8] * 1e3, 2),
         "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
         "useful_bytes": ub,
         "flops": flops(w.H, w.D, w.sq, sum_len),
-        "split_us": round(split_avg * 1e3, 2),
-        "merge_us": round(statistics.fmean(merge_ms) * 1e3, 2),
         "warm_cache_us_per_step": round(statistics.median(warm) * 1e3, 2),
         "wall_ms_per_step_incl_sweep": round(wall / K * 1e3, 4),
         "max_abs_err_vs_oracle_b0": parity,
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_valu" if plan["path"] == 1 else "split_mfma",
+            "kernel": "decode_valu" if plan["path"] == 1 else "decode_mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -49,16 +49,14 @@ class Shape(ctypes.Structure):
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("split_done_event", ctypes.c_void_p),
-                ("reserved", ctypes.c_int32 * 4)]
+    _fields_ = [("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class PlanInfo(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("max_chunks", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
-                ("row_blocks", ctypes.c_int32), ("split_grid", ctypes.c_int32),
-                ("combine_grid", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("rows_per_group", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
+                ("row_block", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -124,21 +122,18 @@ def make_shape(B, H, G, sq, T, D, q_dtype=GQA_BF16, kv_dtype=GQA_BF16, out_dtype
     return Shape(B, H, G, sq, T, D, q_dtype, kv_dtype, out_dtype)
 
 
-def _options(path=PATH_AUTO, chunk_tokens=0, split_done_event=None):
+def _options(path=PATH_AUTO, workgroups=0):
     o = Options()
     o.path = int(path)
-    o.chunk_tokens = int(chunk_tokens)
-    if split_done_event is not None:
-        # a torch.cuda.Event: its hipEvent_t handle (created on first use)
-        o.split_done_event = ctypes.c_void_p(split_done_event.cuda_event)
+    o.workgroups = int(workgroups)
     return o
 
 
-def plan(shape: Shape, path=PATH_AUTO, chunk_tokens=0) -> dict:
+def plan(shape: Shape, path=PATH_AUTO, workgroups=0) -> dict:
     """The planner's launch decisions for ``shape`` (host only)."""
     lib = load_library()
     info = PlanInfo()
-    opts = _options(path, chunk_tokens)
+    opts = _options(path, workgroups)
     _check(lib.gqa_plan(ctypes.byref(shape), ctypes.byref(opts), ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
 
@@ -160,16 +155,14 @@ def shape_of(q, k_cache, out_dtype=None) -> Shape:
 
 
 def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
-           path=PATH_AUTO, chunk_tokens=0, workspace=None, stream=None,
-           split_done_event=None):
+           path=PATH_AUTO, workgroups=0, workspace=None, stream=None):
     """Grouped-query attention for one decode step (see module docstring).
 
     Runs asynchronously on ``stream`` (default: torch's current stream).
-    ``workspace``: optional uint8 CUDA tensor of at least
-    ``workspace_bytes(shape_of(q, k_cache))`` bytes; default: library-owned.
-    ``split_done_event``: optional torch.cuda.Event (created with
-    ``enable_timing=True`` and already recorded once, so that its handle
-    exists) that the library records between its split and merge kernels.
+    ``workspace``: optional uint8 GPU tensor of at least
+    ``workspace_bytes(shape_of(q, k_cache))`` bytes, zero-filled before its
+    first use (each call leaves it zeroed); default: library-owned.
+    ``workgroups``: kernel grid size (0 = the planner's choice).
     """
     import torch
     lib = load_library()
@@ -203,7 +196,7 @@ def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    opts = _options(path, chunk_tokens, split_done_event)
+    opts = _options(path, workgroups)
     ws_ptr, ws_len = None, 0
     if workspace is not None:
         if not workspace.is_cuda or workspace.device != dev:

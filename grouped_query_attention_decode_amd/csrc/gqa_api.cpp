@@ -1,5 +1,5 @@
 // gqa_api.cpp -- the C ABI of libgqa (include/gqa.h): argument checks, the
-// chunk planner, the library-owned workspace and the launch.
+// work planner, the library-owned workspace and the launch.
 //
 // The checks follow the shape rules of "GQA (Grouped-Query Attention) 분석",
 // section "Tensor parallelism과 kernel 제약" (head dims must agree and H must
@@ -44,6 +44,19 @@ int pow2_ceil(int x)
     return p;
 }
 
+int device_compute_units()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;                          // MI355X
+    }
+    return n;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
 // Validate the shape and options and build the launch plan.
 gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* p)
 {
@@ -61,60 +74,57 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
                     s->q_dtype, s->kv_dtype, s->out_dtype);
     if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
         return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
+    if ((int64_t)s->B * s->H * s->sq * s->D >= (int64_t)1 << 40)
+        return fail(GQA_ERR_INVALID_ARG, "B * H * sq * D too large");
     const int64_t R64 = (int64_t)(s->H / s->G) * s->sq;
     if (R64 > (1 << 20)) return fail(GQA_ERR_INVALID_ARG, "(H/G)*sq too large");
-    int path_req = GQA_PATH_AUTO, chunk_req = 0;
+    int path_req = GQA_PATH_AUTO, wg_req = 0;
     if (o) {
         path_req = o->path;
-        chunk_req = o->chunk_tokens;
-        for (int i = 0; i < 4; ++i)
+        wg_req = o->workgroups;
+        for (int i = 0; i < 6; ++i)
             if (o->reserved[i] != 0) return fail(GQA_ERR_INVALID_ARG, "options.reserved must be zero");
         if (path_req < GQA_PATH_AUTO || path_req > GQA_PATH_MFMA)
             return fail(GQA_ERR_INVALID_ARG, "unknown path %d", path_req);
-        if (chunk_req < 0) return fail(GQA_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
+        if (wg_req < 0) return fail(GQA_ERR_INVALID_ARG, "workgroups must be >= 0");
     }
-    if (path_req == GQA_PATH_MFMA)
-        return fail(GQA_ERR_UNSUPPORTED, "the MFMA path is not built in this version");
+    if (path_req == GQA_PATH_MFMA && !bf16)
+        return fail(GQA_ERR_UNSUPPORTED, "the MFMA path needs bf16 q/k/v");
 
     const int R = (int)R64;
-    p->path = gqa::Path::VALU;
+    // bf16 scores go to the matrix cores; fp32 (or a forced VALU path) stays
+    // on the vector ALU
+    const bool mfma = bf16 && path_req != GQA_PATH_VALU;
+    p->path = mfma ? gqa::Path::MFMA : gqa::Path::VALU;
     p->kv_bf16 = bf16 ? 1 : 0;
     p->D = s->D;
     p->R = R;
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
+    if (mfma && p->row_block < 4) p->row_block = 4;   // one k group of the 16x16 tile
     p->n_rb = (R + p->row_block - 1) / p->row_block;
+    if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
+        return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
+                    p->row_block, (long long)s->B * s->G * p->n_rb, gqa::kMaxSegments);
 
-    // Chunk size: a multiple of the workgroup tile; as large as LDS allows
-    // (scores of chunk * row_block floats <= 32 KB) unless that leaves fewer
-    // than kTargetSplitGroups workgroups, then halved down to one tile.
-    const int tile = gqa::split_tile_rows(p->path, p->kv_bf16, s->D);
-    int ct_max = 8192 / p->row_block;
-    if (ct_max > 2048) ct_max = 2048;
-    ct_max = (ct_max / tile) * tile;
-    if (ct_max < tile) ct_max = tile;
-    const int64_t units = (int64_t)s->B * s->G * p->n_rb;
-    int ct;
-    if (chunk_req > 0) {
-        ct = ((chunk_req + tile - 1) / tile) * tile;
-        if (ct > ct_max) ct = ct_max;
-    } else {
-        ct = tile;
-        while (ct * 2 <= ct_max) ct *= 2;
-        while (ct > tile && units * ((s->T + ct - 1) / ct) < gqa::kTargetSplitGroups) ct /= 2;
-        if (ct % tile) ct = tile;   // keep a whole number of tiles
-    }
-    // one chunk covering the whole cache when the cache is no longer than a tile
-    p->chunk = ct;
-    p->max_chunks = (s->T + ct - 1) / ct;
-    p->split_grid = units * p->max_chunks;
-    if (p->split_grid > 0x7FFFFFFF) return fail(GQA_ERR_INVALID_ARG, "problem too large for one launch");
-    const int64_t rows = (int64_t)s->B * s->H * s->sq;
-    p->combine_grid = p->max_chunks > 1 ? (rows + 3) / 4 : 0;
-    const int lds_main = (ct * p->row_block > gqa::kSplitWaves * p->row_block * s->D)
-                             ? ct * p->row_block
-                             : gqa::kSplitWaves * p->row_block * s->D;
-    p->lds_bytes = (size_t)(lds_main + 2 * p->row_block) * sizeof(float);
-    p->ws_bytes = p->max_chunks > 1 ? (size_t)rows * p->max_chunks * (s->D + 1) * sizeof(float) : 0;
+    // Persistent grid of one-wave workgroups: as many as the GPU holds at
+    // once, each taking an equal share of the cache rows; fewer when the
+    // cache is so small that a share would drop below two tiles.
+    const int64_t max_units = (int64_t)s->B * s->G * p->n_rb * s->T;
+    const int64_t min_share = 2 * (int64_t)gqa::cache_rows_per_wave_tile(*p);
+    // One-wave workgroups: kWavesPerCU per compute unit (fewer if they do not
+    // fit) -- enough loads in flight to saturate HBM; more waves only add
+    // pieces, and so partials and merges.
+    int occ = gqa::resident_groups_per_cu(*p);
+    if (occ <= 0 || occ > gqa::kWavesPerCU) occ = gqa::kWavesPerCU;
+    int64_t P = (int64_t)device_compute_units() * occ;
+    const int64_t by_size = (max_units + min_share - 1) / min_share;
+    if (P > by_size) P = by_size;
+    if (wg_req > 0) P = wg_req;
+    if (P > (1 << 20)) P = 1 << 20;
+    if (P < 1) P = 1;
+    p->grid = s->B > 0 ? P : 0;
+    p->part_bytes = round_up((size_t)P * 2 * (p->row_block * s->D + 16) * sizeof(float), 256);
+    p->ws_bytes = gqa::kCounterRegion + p->part_bytes;
     return GQA_OK;
 }
 
@@ -153,6 +163,10 @@ gqa_status_t library_workspace(size_t need, void** out)
             (void)hipGetLastError();
             return fail(GQA_ERR_ALLOC, "hipMalloc(%zu) for the workspace: %s", grow, hipGetErrorString(e));
         }
+        // the arrival counters must start at zero; every call leaves them zero
+        e = hipMemset(w.ptr, 0, grow);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail(GQA_ERR_HIP, "zeroing the workspace: %s", hipGetErrorString(e));
         w.bytes = grow;
     }
     *out = w.ptr;
@@ -189,9 +203,8 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.v = v;
     a.seq_lens = seq_lens;
     a.out = static_cast<float*>(out);
-    const size_t rows = (size_t)shape->B * shape->H * shape->sq;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = workspace ? a.part_o + rows * plan.max_chunks * shape->D : nullptr;
+    a.counters = static_cast<int32_t*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterRegion);
     a.B = shape->B;
     a.H = shape->H;
     a.G = shape->G;
@@ -199,8 +212,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.T = shape->T;
     a.scale_log2 = scale * 1.4426950408889634f;
 
-    hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream),
-                                      opts ? static_cast<hipEvent_t>(opts->split_done_event) : nullptr);
+    hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -248,12 +260,10 @@ gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_p
     if (st != GQA_OK) return st;
     std::memset(plan, 0, sizeof(*plan));
     plan->path = p.path == gqa::Path::MFMA ? GQA_PATH_MFMA : GQA_PATH_VALU;
-    plan->chunk_tokens = p.chunk;
-    plan->max_chunks = p.max_chunks;
+    plan->workgroups = (int32_t)p.grid;
     plan->rows_per_group = p.R;
     plan->row_blocks = p.n_rb;
-    plan->split_grid = (int32_t)p.split_grid;
-    plan->combine_grid = (int32_t)p.combine_grid;
+    plan->row_block = p.row_block;
     plan->workspace_bytes = p.ws_bytes;
     return ok();
 }

@@ -8,14 +8,15 @@
 
 namespace gqa {
 
-constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kSplitWaves = 4;     // waves per split workgroup
+constexpr int kWave = 64;          // CDNA wavefront width; one wave per workgroup
 constexpr int kSlotsPerLane = 4;   // cache rows one lane loads per tile (VALU)
-constexpr int kMaxRowBlock = 16;   // query rows per VALU workgroup
-constexpr int kMfmaRows = 16;      // query rows per MFMA row tile
-constexpr int kMfmaMaxRows = 64;   // query rows one MFMA workgroup holds
-constexpr int kMfmaTile = 32;      // cache rows per MFMA wave tile
-constexpr int kTargetSplitGroups = 2048;  // planner aims for this many workgroups
+constexpr int kMaxRowBlock = 16;   // query rows per VALU segment
+constexpr int kMaxSegments = 1 << 18;  // (sequence, KV head, row block) triples per call
+constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (measured best)
+// The workspace starts with one arrival counter per possible segment, at a
+// fixed place whatever the shape, so counters never land on another call's
+// partials; the partials follow.
+constexpr size_t kCounterRegion = (size_t)kMaxSegments * sizeof(int32_t);
 
 enum class Path : int { VALU = 1, MFMA = 2 };
 
@@ -24,14 +25,11 @@ struct Plan {
     int kv_bf16;        // 1: bf16 q/k/v, 0: fp32
     int D;
     int R;              // (H/G)*sq query rows per KV head
-    int row_block;      // rows per workgroup (VALU: power of two <= 16; MFMA: 16/32/64)
+    int row_block;      // rows per segment (VALU: power of two <= 16)
     int n_rb;           // row blocks per (b, g)
-    int chunk;          // cache rows per workgroup
-    int max_chunks;     // ceil(T / chunk)
-    int64_t split_grid; // B * G * n_rb * max_chunks
-    int64_t combine_grid;
-    size_t lds_bytes;   // dynamic LDS of the split kernel
-    size_t ws_bytes;    // partial outputs + log-sum-exp
+    int64_t grid;       // workgroups (one wave each) P
+    size_t part_bytes;  // partials: P * 2 * (row_block * D + 16) floats
+    size_t ws_bytes;    // kCounterRegion + part_bytes
 };
 
 struct Args {
@@ -40,19 +38,19 @@ struct Args {
     const void* v;
     const int32_t* seq_lens;
     float* out;
-    float* part_o;      // [B*H*sq, max_chunks, D]
-    float* part_lse;    // [B*H*sq, max_chunks]
+    float* part;        // [P][2] slots: row_block rows of D values, then 16 lse floats
+    int32_t* counters;  // [kMaxSegments], zero before and after every call
     int B, H, G, sq, T;
     float scale_log2;   // scale * log2(e): scores kept in base-2 exponent units
 };
 
-// Queue the split kernel (and the merge kernel when chunks > 1).  When
-// split_done is not null it is recorded on stream between the two.
-hipError_t launch_decode(const Plan& plan, const Args& args, hipStream_t stream,
-                         hipEvent_t split_done);
+// Queue the decode kernel on stream.
+hipError_t launch_decode(const Plan& plan, const Args& args, hipStream_t stream);
 
-// Tile geometry the planner needs: cache rows a whole split workgroup
-// covers per iteration, for the given path / dtype / head dim.
-int split_tile_rows(Path path, int kv_bf16, int D);
+// Workgroups of the plan's kernel one compute unit can hold (0 if unknown).
+int resident_groups_per_cu(const Plan& plan);
+
+// Cache rows one wave covers per tile.
+int cache_rows_per_wave_tile(const Plan& plan);
 
 }  // namespace gqa

@@ -13,20 +13,27 @@
 // same row order, r = g * q_len + s).  Each K/V byte is fetched from HBM once
 // for all R rows; no repeated K/V exists anywhere.
 //
-// Split pass, one workgroup per (b, g, row block, chunk of cache rows):
-//   1. K pass: 16-byte coalesced loads of the chunk's K rows; dot products
-//      with the R query rows; lane-exchange reduce-scatter (DPP) so that each
-//      lane ends with whole scores; scores (in base-2 exponent units) to LDS.
-//   2. Softmax over the chunk in LDS: per-row max, p = 2^(s - max), sum.
-//   3. V pass: 16-byte coalesced loads of the chunk's V rows; acc += p * v.
-//   4. Cross-lane / cross-wave sum; chunk output normalised by its own sum.
-//      A sequence with one chunk writes out directly; otherwise the chunk's
-//      (output, log2-sum-exp) goes to the workspace.
-// Merge pass, one wave per output row: weights 2^(lse_c - max_c lse) in chunk
-// order (deterministic), out = sum_c w_c o_c / sum_c w_c.
+// Work split (one persistent launch, no second kernel):
+//   A "segment" is one (sequence b, KV head g, row block) with L_b cache rows.
+//   All segments laid end to end form W = sum_b L_b * G * row_blocks units of
+//   work; workgroup p of P takes the units [p*W/P, (p+1)*W/P), i.e. the same
+//   number of cache rows for every workgroup however ragged seq_lens is.
+//   Each workgroup reads seq_lens itself to find its pieces, so the host never
+//   reads device memory.
+// A workgroup is one wave.  Per piece (a run of cache rows of one segment)
+// the wave streams tiles of 16-byte coalesced K and V loads, with the next
+// two tiles' loads in flight while the current one is computed, and keeps an
+// online softmax (running max and sum) per query row.  A segment held by one
+// workgroup is written to out directly.
+// A segment cut between workgroups leaves one (output, log2-sum-exp) partial
+// per piece in the workspace; the workgroup that finishes last (per-segment
+// arrival counter) merges the pieces in piece order -- deterministic -- with
+// weights 2^(lse_k - max lse) and resets the counter to zero, so every call
+// leaves the counters as it found them.
 //
-// Split-then-merge is an exact rewrite of one softmax over all rows (the
-// log-sum-exp identity; the oracle pins check it in float64).
+// Splitting the softmax into pieces and merging them by log-sum-exp is an
+// exact rewrite of one softmax over all rows (the oracle pins check this in
+// float64).
 
 #include <math.h>
 #include <stdint.h>
@@ -49,15 +56,15 @@ __device__ __forceinline__ float xchg(float x)
     const int xi = __builtin_bit_cast(int, x);
     int r;
     if constexpr (M == 1) {
-        r = __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true);
     } else if constexpr (M == 2) {
-        r = __builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true);
     } else if constexpr (M == 7) {
-        r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xF, 0xF, true);
     } else if constexpr (M == 15) {
-        r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(xi, 0x140, 0xF, 0xF, true);
     } else if constexpr (M == 8) {
-        r = __builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, true);
     } else if constexpr (M == 4 || M == 16) {
         r = __builtin_amdgcn_ds_swizzle(xi, 0x1F | (M << 10));
     } else {
@@ -194,279 +201,1002 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int T)
     return L < 0 ? 0 : (L > T ? T : L);
 }
 
-// ---------------------------------------------------------------------------
-// Split pass, vector-ALU form.
-//   FMT : Bf16 or F32 (q, k, v share it)
-//   D   : head dim (64 or 128)
-//   RB  : query rows per workgroup (1, 2, 4, 8, 16)
-// Grid: B * G * n_rb * max_chunks workgroups of kSplitWaves waves.
-// Dynamic LDS: max(chunk * RB, kSplitWaves * RB * D) floats + 2 * RB floats.
-// ---------------------------------------------------------------------------
-template <class FMT, int D, int RB>
-__global__ void __launch_bounds__(kSplitWaves * kWave)
-split_valu(const Args a, const int R, const int n_rb, const int chunk, const int max_chunks)
+// Max / sum over the lane bits LO..5 (exact xor partners): lanes that differ
+// only in those bits end with the same result.
+template <int LO>
+__device__ __forceinline__ float lanes_max(float x)
 {
-    constexpr int ES = FMT::kBytes;
-    constexpr int EPL = FMT::kPerLoad;        // elements per 16-byte load
-    constexpr int LPT = D * ES / 16;          // lanes covering one cache row
-    constexpr int TPL = kWave / LPT;          // cache rows per wave-wide load
-    constexpr int NL = kSlotsPerLane;         // rows per lane per tile
-    constexpr int TW = NL * TPL;              // cache rows per wave tile
-    constexpr int NW = kSplitWaves;
-    constexpr int NV = NL * RB;               // partial dots per lane per tile
-    constexpr int NSC = NV >= LPT ? NV / LPT : 1;   // whole scores per lane
-    constexpr int NA = RB * EPL;              // accumulators per lane
-    constexpr int NAK = NA / TPL;             // accumulators kept after the lane-group sum
-    static_assert(LPT >= 1 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row lanes");
-    static_assert(NA >= TPL, "accumulator scatter needs RB * D >= 64");
+    if constexpr (LO <= 0) x = fmaxf(x, xchg<1>(x));
+    if constexpr (LO <= 1) x = fmaxf(x, xchg<2>(x));
+    if constexpr (LO <= 2) x = fmaxf(x, xchg<4>(x));
+    if constexpr (LO <= 3) x = fmaxf(x, xchg<8>(x));
+    if constexpr (LO <= 4) x = fmaxf(x, xchg<16>(x));
+    if constexpr (LO <= 5) x = fmaxf(x, xchg<32>(x));
+    return x;
+}
 
-    extern __shared__ float smem[];
-    float* s_lds = smem;                      // [chunk][RB] scores, then p
-    const int lds_main = (chunk * RB > NW * RB * D) ? chunk * RB : NW * RB * D;
-    float* row_m = smem + lds_main;           // [RB] chunk max (base-2 units)
-    float* row_l = row_m + RB;                // [RB] chunk sum of p
-    float* red = smem;                        // [NW][RB][D], reuses s_lds at the end
+template <int LO>
+__device__ __forceinline__ float lanes_sum(float x)
+{
+    if constexpr (LO <= 0) x += xchg<1>(x);
+    if constexpr (LO <= 1) x += xchg<2>(x);
+    if constexpr (LO <= 2) x += xchg<4>(x);
+    if constexpr (LO <= 3) x += xchg<8>(x);
+    if constexpr (LO <= 4) x += xchg<16>(x);
+    if constexpr (LO <= 5) x += xchg<32>(x);
+    return x;
+}
 
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Compiler-level fence for LDS traffic private to one wave: the hardware
+// executes one wave's LDS operations in order; this keeps the compiler from
+// moving them across each other.
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t xchg_u(uint32_t x)
+{
+    return __builtin_bit_cast(uint32_t, xchg<M>(__builtin_bit_cast(float, x)));
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x)
+{
+    x += xchg_u<15>(x);
+    x += xchg_u<7>(x);
+    x += xchg_u<2>(x);
+    x += xchg_u<1>(x);
+    x += xchg_u<16>(x);
+    x += xchg_u<32>(x);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Equal-work schedule.  Work units: cache rows of all segments, segments in
+// order (b, g, row block).  Workgroup p owns units [start(p), start(p+1)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long long wg_start(long long W, int P, int p)
+{
+    return (long long)p * W / P;
+}
+
+// The workgroup whose range holds unit x (0 <= x < W).
+__device__ __forceinline__ int wg_of(long long x, long long W, int P)
+{
+    return (int)(((x + 1) * P - 1) / W);
+}
+
+// This workgroup's share of the work; every lane holds the same values.
+struct Sched {
+    long long total;     // W
+    long long first_b;   // first sequence this workgroup touches
+    long long first_e;   // units before that sequence
+};
+
+// W = units_per_seq * sum_b clamp(L_b); then the first sequence whose units
+// reach past this workgroup's start.  Executed by all 64 lanes of the wave.
+__device__ __forceinline__ Sched schedule_wave(const Args& a, int units_per_seq, int P, int p)
+{
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-
-    int bid = blockIdx.x;
-    const int c = bid % max_chunks;
-    bid /= max_chunks;
-    const int rb = bid % n_rb;
-    bid /= n_rb;
-    const int g = bid % a.G;
-    const int b = bid / a.G;
-
-    const int L = clamp_len(a.seq_lens, b, a.T);
-    const int nc = (L + chunk - 1) / chunk;
-    if (c > 0 && c >= nc) return;             // empty chunk (chunk 0 always runs)
-    const int t0 = c * chunk;
-    const int t1 = min(t0 + chunk, L);        // may be <= t0 when L == 0
-    const int row0 = rb * RB;
-    const int sq = a.sq;
-
-    // Query rows of this block (contiguous in q); lane holds its 16-byte slice.
-    const int dslot = lane % LPT;
-    const int doff = dslot * EPL;
-    const int64_t qrow0 = (int64_t)b * a.H * sq + (int64_t)g * R + row0;
-    uint4 qv[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        if (row0 + i < R)
-            qv[i] = load16(static_cast<const char*>(a.q) + ((qrow0 + i) * D + doff) * ES);
-        else
-            qv[i] = make_uint4(0, 0, 0, 0);
+    long long tot = 0;
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
+        const int b = b0 + lane;
+        const uint32_t L = b < a.B ? (uint32_t)clamp_len(a.seq_lens, b, a.T) : 0u;
+        tot += wave_sum_u32(L);
     }
-
-    const int64_t slab = ((int64_t)b * a.G + g) * a.T * D;
-    const char* kbase = static_cast<const char*>(a.k) + slab * ES;
-    const char* vbase = static_cast<const char*>(a.v) + slab * ES;
-    const int lrow = lane / LPT;              // which of the TPL rows of a load
-
-    // ---- 1. K pass --------------------------------------------------------
-    for (int tb = t0 + wave * TW; tb < t1; tb += NW * TW) {
-        uint4 kv[NL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int t = tb + j * TPL + lrow;
-            kv[j] = (t < t1) ? load16(kbase + ((int64_t)t * D + doff) * ES) : make_uint4(0, 0, 0, 0);
+    Sched s;
+    s.total = tot * units_per_seq;
+    s.first_b = a.B;
+    s.first_e = s.total;
+    const long long A = wg_start(s.total, P, p);
+    long long carry = 0;
+    for (int b0 = 0; b0 < a.B && s.total > 0; b0 += kWave) {
+        const int b = b0 + lane;
+        const uint32_t L = b < a.B ? (uint32_t)clamp_len(a.seq_lens, b, a.T) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(L, lane);
+        const long long end_b = (carry + incl) * units_per_seq;
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && end_b > A);
+        const uint32_t chunk_total = __shfl(incl, kWave - 1);
+        if (hit) {
+            const int f = __builtin_ctzll(hit);
+            s.first_b = b0 + f;
+            s.first_e = (carry + __shfl(incl - L, f)) * units_per_seq;
+            break;
         }
-        float part[NV];
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-#pragma unroll
-            for (int i = 0; i < RB; ++i) part[j * RB + i] = FMT::dot(qv[i], kv[j], 0.0f);
-        reduce_scatter<NV, LPT / 2, 1, true>(part, lane);
-        const bool writer = (NV >= LPT) || (dslot % (LPT / (NV < LPT ? NV : LPT)) == 0);
-        if (writer) {
-            const int base = (NV >= LPT) ? dslot * NSC : dslot / (LPT / (NV < LPT ? NV : LPT));
-#pragma unroll
-            for (int m = 0; m < NSC; ++m) {
-                const int idx = base + m;
-                const int j = idx / RB;
-                const int i = idx % RB;
-                const int t = tb + j * TPL + lrow;
-                const int r = row0 + i;
-                const bool vis = (t < t1) && (r < R) && (t <= L - sq + (r % sq));
-                s_lds[(t - t0) * RB + i] = vis ? part[m] * a.scale_log2 : -INFINITY;
-            }
-        }
+        carry += chunk_total;
     }
-    __syncthreads();
+    return s;
+}
 
-    // ---- 2. softmax over this chunk, one wave per row ----------------------
-    const int nt = t1 > t0 ? t1 - t0 : 0;
-    for (int i = wave; i < RB; i += NW) {
-        float mx = -INFINITY;
-        for (int t = lane; t < nt; t += kWave) mx = fmaxf(mx, s_lds[t * RB + i]);
-        mx = wave_max(mx);
-        float sum = 0.0f;
-        for (int t = lane; t < nt; t += kWave) {
-            const float p = (mx == -INFINITY) ? 0.0f : exp2f(s_lds[t * RB + i] - mx);
-            s_lds[t * RB + i] = p;
-            sum += p;
-        }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            row_m[i] = mx;
-            row_l[i] = sum;
-        }
+// Partials cross workgroups that may run on different XCDs, whose L2 caches
+// are not coherent with each other.  They are written and read through a
+// buffer resource with the device-scope cache policy (SC1): stores write
+// through to, and loads read from, the device-coherent level, so no fence
+// has to write back or invalidate a whole L2 (which would also throw away
+// the K/V lines other waves are streaming), and -- unlike atomic loads --
+// the loads of a merge can all be in flight at once.
+constexpr int kCoherent = 16;                // SC1 cache-policy bit
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* base)
+{
+    // raw (untyped) buffer, no swizzle, 2 GiB - 1 byte range
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int index, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, index * 4, 0, kCoherent);
+}
+
+__device__ __forceinline__ float load_coherent(__amdgpu_buffer_rsrc_t r, int index)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, kCoherent));
+}
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Four consecutive floats (index a multiple of 4): one 16-byte access, so a
+// written-through line is not split into many small writes.
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, int index, const float* v)
+{
+    const u32x4_t x = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, index * 4, 0, kCoherent);
+}
+
+__device__ __forceinline__ void load4_coherent(__amdgpu_buffer_rsrc_t r, int index, float* v)
+{
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, index * 4, 0, kCoherent);
+    v[0] = __uint_as_float(x[0]);
+    v[1] = __uint_as_float(x[1]);
+    v[2] = __uint_as_float(x[2]);
+    v[3] = __uint_as_float(x[3]);
+}
+
+// A segment for which this wave left a partial; merged once every piece has
+// arrived.
+struct Pending {
+    int seg;          // arrival counter index
+    int p_first;      // first workgroup holding a piece of the segment
+    int npieces;
+    long long off;    // the segment's first work unit
+    int64_t qrow0;    // output row of the segment's first query row
+    int row0;         // first query row of the segment within its KV head
+};
+
+// Partial slot of workgroup q for the segment starting at unit off: slot 0
+// when the segment holds q's first unit, else slot 1 (the segment that runs
+// past q's last unit).  A slot is RB rows of D values (16-byte aligned) and
+// then RB log2-sum-exp values padded to 16 floats; offset in floats.
+template <int D, int RB>
+__device__ __forceinline__ int slot_base(int q, long long off, long long W, int P)
+{
+    return (q * 2 + (wg_start(W, P, q) >= off ? 0 : 1)) * (RB * D + 16);
+}
+
+// End of a piece, for one wave.  row_m / row_l (LDS) hold each row's max and
+// sum over the piece; acc[m] is the weighted V sum of query row u / EPL,
+// element doff + u % EPL, for u = ubase + m.  Writes out directly when the
+// segment lies in this workgroup; else stores the partial (output / sum and
+// log2-sum-exp) and fills *pd.  Returns whether a partial was left.  Issues
+// stores only -- nothing waits here.
+template <int D, int RB, int EPL, int NAK>
+__device__ __forceinline__ bool piece_output(const Args& a, const float* row_m, const float* row_l,
+                                             const float* acc, int ubase, int doff, int64_t qrow0,
+                                             int row0, int R, int n_rb, int b, int g, int rb,
+                                             long long off, int L, long long W, int P, int p,
+                                             Pending* pd)
+{
+    const int p_first = wg_of(off, W, P);
+    const int npieces = wg_of(off + L - 1, W, P) - p_first + 1;
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int mine = slot_base<D, RB>(p, off, W, P);
+    float val[NAK];
+#pragma unroll
+    for (int m = 0; m < NAK; ++m) {
+        const int i = (ubase + m) / EPL;
+        const float l = row_l[i];
+        val[m] = l > 0.0f ? acc[m] / l : 0.0f;
     }
-    __syncthreads();
-
-    // ---- 3. V pass ------------------------------------------------------------
-    float acc[NA];
-#pragma unroll
-    for (int u = 0; u < NA; ++u) acc[u] = 0.0f;
-    for (int tb = t0 + wave * TW; tb < t1; tb += NW * TW) {
-        uint4 vv[NL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int t = tb + j * TPL + lrow;
-            vv[j] = (t < t1) ? load16(vbase + ((int64_t)t * D + doff) * ES) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int t = tb + j * TPL + lrow;
-            float pr[RB];
-#pragma unroll
-            for (int i = 0; i < RB; ++i) pr[i] = (t < t1) ? s_lds[(t - t0) * RB + i] : 0.0f;
-            float vf[EPL];
-            FMT::unpack(vv[j], vf);
-#pragma unroll
-            for (int i = 0; i < RB; ++i)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[i * EPL + e] = fmaf(pr[i], vf[e], acc[i * EPL + e]);
-        }
-    }
-
-    // ---- 4. sum over the TPL row groups of the wave, then over waves ---------
-    reduce_scatter<NA, kWave / 2, LPT, false>(acc, lane);
-    __syncthreads();                          // s_lds is reused as red[] below
-    {
-        const int ubase = lrow * NAK;
+    if (npieces == 1) {
 #pragma unroll
         for (int m = 0; m < NAK; ++m) {
             const int u = ubase + m;
             const int i = u / EPL;
-            const int e = u % EPL;
-            red[(wave * RB + i) * D + doff + e] = acc[m];
+            if (row0 + i < R) a.out[(qrow0 + i) * D + doff + u % EPL] = val[m];
         }
+        return false;
     }
-    __syncthreads();
-
-    const bool direct = nc <= 1;
-    for (int idx = threadIdx.x; idx < RB * D; idx += NW * kWave) {
-        const int i = idx / D;
-        const int d = idx % D;
-        const int r = row0 + i;
-        if (r >= R) continue;
-        float o = 0.0f;
+    // a lane's accumulators are runs of consecutive elements of one row
+    if constexpr (NAK % 4 == 0 && EPL % 4 == 0) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) o += red[(w * RB + i) * D + d];
-        const float l = row_l[i];
-        const float val = l > 0.0f ? o / l : 0.0f;
-        const int64_t orow = qrow0 + i;
-        if (direct) {
-            a.out[orow * D + d] = val;
-        } else {
-            a.part_o[(orow * max_chunks + c) * D + d] = val;
-            if (d == 0) a.part_lse[orow * max_chunks + c] = l > 0.0f ? row_m[i] + log2f(l) : -INFINITY;
+        for (int m = 0; m < NAK; m += 4) {
+            const int u = ubase + m;
+            store4_coherent(part, mine + (u / EPL) * D + doff + u % EPL, &val[m]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NAK; ++m) {
+            const int u = ubase + m;
+            store_coherent(part, mine + (u / EPL) * D + doff + u % EPL, val[m]);
         }
     }
+#pragma unroll
+    for (int m = 0; m < NAK; ++m) {
+        const int u = ubase + m;
+        const int i = u / EPL;
+        if (doff + u % EPL == 0) {
+            const float l = row_l[i];
+            store_coherent(part, mine + RB * D + i, l > 0.0f ? row_m[i] + log2f(l) : -INFINITY);
+        }
+    }
+    pd->seg = (b * a.G + g) * n_rb + rb;
+    pd->p_first = p_first;
+    pd->npieces = npieces;
+    pd->off = off;
+    pd->qrow0 = qrow0;
+    pd->row0 = row0;
+    return true;
 }
 
-// ---------------------------------------------------------------------------
-// Merge pass: one wave per output row (b, h, s), 4 rows per workgroup.
-// Rows of sequences with at most one chunk were written by the split pass.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256)
-merge_chunks(const Args a, const int chunk, const int max_chunks)
+// Count this wave's arrival for a pending segment; the last arrival merges
+// the pieces' partials in piece order (deterministic) and resets the
+// counter.  The caller must have waited for its own partial stores
+// (s_waitcnt 0), so that the last arrival sees every partial.
+template <int D, int RB, int EPL, int NAK>
+__device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& pd, int lane, int ubase,
+                                                 int doff, int R, long long W, int P)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    const int64_t rows_per_b = (int64_t)a.H * a.sq;
-    if (row >= (int64_t)a.B * rows_per_b) return;
-    const int b = (int)(row / rows_per_b);
-    const int L = clamp_len(a.seq_lens, b, a.T);
-    const int nc = (L + chunk - 1) / chunk;
-    if (nc <= 1) return;
+    constexpr int NR = NAK >= EPL ? NAK / EPL : 1;    // query rows among a lane's accumulators
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != pd.npieces - 1) return;
 
-    const float* lse = a.part_lse + row * max_chunks;
-    float M = -INFINITY;
-    for (int c = lane; c < nc; c += kWave) M = fmaxf(M, lse[c]);
-    M = wave_max(M);
-    const float* po = a.part_o + row * max_chunks * D;
-    for (int d = lane; d < D; d += kWave) {
-        float num = 0.0f, den = 0.0f;
-        if (M != -INFINITY) {
-            for (int c = 0; c < nc; ++c) {
-                const float w = exp2f(lse[c] - M);
-                num = fmaf(w, po[(int64_t)c * D + d], num);
-                den += w;
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int i0 = ubase / EPL;
+    float M[NR], den[NR], num[NAK];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        M[r] = -INFINITY;
+        den[r] = 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < NAK; ++m) num[m] = 0.0f;
+    for (int k0 = 0; k0 < pd.npieces; k0 += 4) {
+        // the loads of four pieces are in flight together
+        float lse[4][NR], ov[4][NAK];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int base = slot_base<D, RB>(pd.p_first + min(k0 + kk, pd.npieces - 1), pd.off, W, P);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) lse[kk][r] = load_coherent(part, base + RB * D + i0 + r);
+            if constexpr (NAK % 4 == 0 && EPL % 4 == 0) {
+#pragma unroll
+                for (int m = 0; m < NAK; m += 4) {
+                    const int u = ubase + m;
+                    load4_coherent(part, base + (u / EPL) * D + doff + u % EPL, &ov[kk][m]);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < NAK; ++m) {
+                    const int u = ubase + m;
+                    ov[kk][m] = load_coherent(part, base + (u / EPL) * D + doff + u % EPL);
+                }
             }
         }
-        a.out[row * D + d] = den > 0.0f ? num / den : 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (k0 + kk >= pd.npieces) break;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                // running log-sum-exp merge, in piece order
+                const float x = lse[kk][r];
+                if (x == -INFINITY) continue;
+                const float Mn = fmaxf(M[r], x);
+                const float sc = __builtin_amdgcn_exp2f(M[r] - Mn);
+                const float w = __builtin_amdgcn_exp2f(x - Mn);
+                den[r] = fmaf(den[r], sc, w);
+                M[r] = Mn;
+#pragma unroll
+                for (int m = 0; m < NAK; ++m)
+                    if ((ubase + m) / EPL == i0 + r) num[m] = fmaf(num[m], sc, w * ov[kk][m]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NAK; ++m) {
+        const int u = ubase + m;
+        const int i = u / EPL;
+        if (pd.row0 + i >= R) continue;
+        const float dd = den[i - i0];
+        a.out[(pd.qrow0 + i) * D + doff + u % EPL] = dd > 0.0f ? num[m] / dd : 0.0f;
+    }
+    if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output of a piece, resolving a partial right away (vector-ALU kernel).
+template <int D, int RB, int EPL, int NAK>
+__device__ __forceinline__ void finish_piece(const Args& a, const float* row_m, const float* row_l,
+                                             const float* acc, int lane, int ubase, int doff,
+                                             int64_t qrow0, int row0, int R, int n_rb, int b, int g,
+                                             int rb, long long off, int L, long long W, int P, int p)
+{
+    Pending pd;
+    if (piece_output<D, RB, EPL, NAK>(a, row_m, row_l, acc, ubase, doff, qrow0, row0, R, n_rb, b, g, rb,
+                                      off, L, W, P, p, &pd)) {
+        __builtin_amdgcn_s_waitcnt(0);       // own partial stores complete at device scope
+        arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, ubase, doff, R, W, P);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers
+// Split pass, vector-ALU form.  One wave per workgroup: every wave is an
+// independent worker with its own share of the work, so no barrier ever
+// stalls a compute unit -- while one wave is at a piece boundary the others
+// keep streaming.
+//   FMT : Bf16 or F32 (q, k, v share it)
+//   D   : head dim (64 or 128)
+//   RB  : query rows per segment (1, 2, 4, 8, 16)
+//
+// Lane layout for one wave-wide 16-byte load: lane = lrow * LPT + dslot,
+// cache row = tile + j * TPL + lrow (j = 0..NL-1 slots), elements
+// dslot * EPL .. + EPL.  After the K dot products and the reduce-scatter a
+// lane holds NSC whole scores; score index idx = j * RB + i (row i).
 // ---------------------------------------------------------------------------
-int split_tile_rows(Path path, int kv_bf16, int D)
+template <class FMT, int D, int RB>
+struct ValuGeom {
+    static constexpr int ES = FMT::kBytes;
+    static constexpr int EPL = FMT::kPerLoad;        // elements per 16-byte load
+    static constexpr int LPT = D * ES / 16;          // lanes covering one cache row
+    static constexpr int TPL = kWave / LPT;          // cache rows per wave-wide load
+    static constexpr int NL = kSlotsPerLane;         // rows per lane per tile
+    static constexpr int TW = NL * TPL;              // cache rows per tile
+    static constexpr int NV = NL * RB;               // partial dots per lane per tile
+    static constexpr int NSC = NV >= LPT ? NV / LPT : 1;    // whole scores per lane
+    static constexpr int REP = NV >= LPT ? 1 : LPT / NV;    // lanes holding the same score
+    static constexpr int ROWLO = ilog2(LPT / NL);    // lane bits >= ROWLO never change a score's row
+    static constexpr int NA = RB * EPL;              // accumulators per lane
+    static constexpr int NAK = NA / TPL;             // accumulators kept after the row-group sum
+    static constexpr int PB = RB * NL;               // p values of one load row group
+    static_assert(LPT >= 1 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row lanes");
+    static_assert(NA >= TPL, "accumulator scatter needs RB * D >= 64");
+};
+
+template <class FMT, int D, int RB>
+struct ValuShared {
+    using Gm = ValuGeom<FMT, D, RB>;
+    uint32_t pbuf[Gm::TPL * Gm::PB];   // p of the current tile, [lrow][j][i]
+    float alpha[RB];                   // per-row rescale factors
+    float row_m[RB];                   // per-row max and sum at the end of a piece
+    float row_l[RB];
+};
+
+// Rows of sequences with no valid cache rows are all zeros; workgroup p
+// writes those of sequences b = p, p + P, ...
+template <int D>
+__device__ void zero_empty_sequences(const Args& a, int P, int p)
 {
-    if (path == Path::MFMA) return kSplitWaves * kMfmaTile;
-    const int es = kv_bf16 ? 2 : 4;
-    const int lpt = D * es / 16;
-    return kSplitWaves * kSlotsPerLane * (kWave / lpt);
+    const int rows = a.H * a.sq;
+    for (int b = p; b < a.B; b += P) {
+        if (clamp_len(a.seq_lens, b, a.T) != 0) continue;
+        float* o = a.out + (int64_t)b * rows * D;
+        for (int idx = threadIdx.x; idx < rows * D; idx += kWave) o[idx] = 0.0f;
+    }
 }
 
-typedef void (*SplitFn)(const Args, int, int, int, int);
+// Walk this workgroup's pieces: fn(b, g, rb, ta, tb, off, Lb) for each.
+template <class Fn>
+__device__ __forceinline__ void for_each_piece(const Args& a, const Sched& sh, int n_rb, int P, int p,
+                                               Fn&& fn)
+{
+    const long long W = sh.total;
+    const long long A = wg_start(W, P, p);
+    const long long E = wg_start(W, P, p + 1);
+    if (A >= E) return;                      // more workgroups than units: nothing here
+    const int units = a.G * n_rb;
+    int b = (int)sh.first_b;
+    long long Eb = sh.first_e;
+    while (b < a.B && Eb < E) {
+        const int Lb = clamp_len(a.seq_lens, b, a.T);
+        if (Lb > 0) {
+            for (long long k = A > Eb ? (A - Eb) / Lb : 0; k < units; ++k) {
+                const long long off = Eb + k * Lb;
+                if (off >= E) break;
+                const int ta = (int)(A > off ? A - off : 0);
+                const int tb = (int)(E - off < Lb ? E - off : Lb);
+                fn(b, (int)(k / n_rb), (int)(k % n_rb), ta, tb, off, Lb);
+            }
+        }
+        Eb += (long long)units * Lb;
+        ++b;
+    }
+}
+
+// Stream cache rows [ta, tb) of segment (b, g, rb) -- one piece -- and
+// finish it: write out directly when the segment lies in this workgroup,
+// else leave a partial and merge all partials if this workgroup arrives last.
+template <class FMT, int D, int RB>
+__device__ __forceinline__ void valu_piece(const Args& a, ValuShared<FMT, D, RB>& sm, int R, int n_rb,
+                                           int b, int g, int rb, int ta, int tb, long long off, int L,
+                                           long long W, int P, int p)
+{
+    using Gm = ValuGeom<FMT, D, RB>;
+    constexpr int ES = Gm::ES, EPL = Gm::EPL, LPT = Gm::LPT, TPL = Gm::TPL, NL = Gm::NL;
+    constexpr int TW = Gm::TW, NV = Gm::NV, NSC = Gm::NSC, REP = Gm::REP;
+    constexpr int ROWLO = Gm::ROWLO, NA = Gm::NA, NAK = Gm::NAK, PB = Gm::PB;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row0 = rb * RB;
+    const int sq = a.sq;
+    const int dslot = lane % LPT;
+    const int doff = dslot * EPL;
+    const int lrow = lane / LPT;
+
+    // rows past R (padding of the last row block) re-read row R-1; their
+    // scores are masked, so the values never matter
+    const int64_t qrow0 = (int64_t)b * a.H * sq + (int64_t)g * R + row0;
+    uint4 qv[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int64_t r = qrow0 + min(i, R - 1 - row0);
+        qv[i] = load16(static_cast<const char*>(a.q) + (r * D + doff) * ES);
+    }
+
+    // rows (and their visibility limit) of the scores this lane holds
+    int my_i[NSC], my_j[NSC], my_last[NSC];
+#pragma unroll
+    for (int m = 0; m < NSC; ++m) {
+        const int idx = (NV >= LPT) ? dslot * NSC + m : dslot / REP;
+        my_i[m] = idx % RB;
+        my_j[m] = idx / RB;
+        const int r = row0 + my_i[m];
+        my_last[m] = (r < R) ? L - sq + (r % sq) : -1;
+    }
+    const bool p_writer = (NV >= LPT) || (dslot % REP == 0);
+    uint32_t* pbuf = sm.pbuf;
+    float* alpha = sm.alpha;
+
+    const int64_t slab = ((int64_t)b * a.G + g) * a.T * D;
+    const char* kbase = static_cast<const char*>(a.k) + slab * ES;
+    const char* vbase = static_cast<const char*>(a.v) + slab * ES;
+
+    float m_run[NSC], l_run[NSC];
+#pragma unroll
+    for (int m = 0; m < NSC; ++m) {
+        m_run[m] = -INFINITY;
+        l_run[m] = 0.0f;
+    }
+    float acc[NA];
+#pragma unroll
+    for (int u = 0; u < NA; ++u) acc[u] = 0.0f;
+
+    // Rows past the piece's end re-read row tb - 1, which is valid: their
+    // scores are masked to -inf and their weights are exactly 0, so no row
+    // at or beyond tb is ever read and no branch guards the loads.
+    auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int t = min(t0 + j * TPL + lrow, tb - 1);
+            const int64_t o = ((int64_t)t * D + doff) * ES;
+            kk[j] = load16(kbase + o);
+            vv[j] = load16(vbase + o);
+        }
+    };
+
+    auto compute_tile = [&](int t0, const uint4* kk, const uint4* vv) {
+        // scores: partial dots, then reduce-scatter within each cache row's lanes
+        float part[NV];
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+#pragma unroll
+            for (int i = 0; i < RB; ++i) part[j * RB + i] = FMT::dot(qv[i], kk[j], 0.0f);
+        reduce_scatter<NV, LPT / 2, 1, true>(part, lane);
+
+        float s[NSC], m_new[NSC];
+        bool grew = false;
+#pragma unroll
+        for (int m = 0; m < NSC; ++m) {
+            const int t = t0 + my_j[m] * TPL + lrow;
+            const bool vis = (t < tb) && (t <= my_last[m]);
+            s[m] = vis ? part[m] * a.scale_log2 : -INFINITY;
+            const float tmax = lanes_max<ROWLO>(s[m]);
+            m_new[m] = fmaxf(m_run[m], tmax);
+            grew |= m_new[m] > m_run[m];
+        }
+        // a row's max grew: rescale that row's sums (rare after the first tiles)
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+            for (int m = 0; m < NSC; ++m) {
+                const float al = (m_new[m] > m_run[m]) ? __builtin_amdgcn_exp2f(m_run[m] - m_new[m]) : 1.0f;
+                l_run[m] *= al;
+                m_run[m] = m_new[m];
+                if (p_writer) alpha[my_i[m]] = al;
+            }
+            wave_lds_fence();
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const float al = alpha[i];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[i * EPL + e] *= al;
+            }
+        }
+        // p = 2^(s - m) in fp32, shared with the lanes of the same cache row group
+#pragma unroll
+        for (int m = 0; m < NSC; ++m) {
+            const float pv = (s[m] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[m] - m_run[m]);
+            l_run[m] += pv;
+            if (p_writer) pbuf[lrow * PB + my_j[m] * RB + my_i[m]] = __float_as_uint(pv);
+        }
+        wave_lds_fence();
+        // weighted V sum, fp32 weights and fp32 accumulation
+        {
+            const float* src = reinterpret_cast<const float*>(pbuf) + lrow * PB;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                float vf[EPL];
+                FMT::unpack(vv[j], vf);
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    const float pv = src[j * RB + i];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[i * EPL + e] = fmaf(pv, vf[e], acc[i * EPL + e]);
+                }
+            }
+        }
+        wave_lds_fence();   // next tile's p writes stay behind these reads
+    };
+
+    // Three register buffers in rotation: the next two tiles are in flight
+    // while the current one is computed.  The loads are issued
+    // unconditionally (rows clamped into the piece): with the same number of
+    // loads on every path the compiler waits for exactly the oldest tile
+    // instead of draining the prefetches.
+    {
+        uint4 ka[NL], va[NL], kb[NL], vb[NL], kc[NL], vc[NL];
+        int t0 = ta;
+        const int ntile = (tb - ta + TW - 1) / TW;
+        load_tile(t0, ka, va);
+        load_tile(t0 + TW, kb, vb);
+        for (int it = 0; it < ntile; it += 3) {
+            load_tile(t0 + 2 * TW, kc, vc);
+            compute_tile(t0, ka, va);
+            t0 += TW;
+            if (it + 1 >= ntile) break;
+            load_tile(t0 + 2 * TW, ka, va);
+            compute_tile(t0, kb, vb);
+            t0 += TW;
+            if (it + 2 >= ntile) break;
+            load_tile(t0 + 2 * TW, kb, vb);
+            compute_tile(t0, kc, vc);
+            t0 += TW;
+        }
+    }
+
+    // ---- end of the piece: sums over the lanes of the wave ------------------
+#pragma unroll
+    for (int m = 0; m < NSC; ++m) l_run[m] = lanes_sum<ROWLO>(l_run[m]);
+    reduce_scatter<NA, kWave / 2, LPT, false>(acc, lane);
+    if (lrow == 0 && p_writer) {
+#pragma unroll
+        for (int m = 0; m < NSC; ++m) {
+            if (my_j[m] == 0) {
+                sm.row_m[my_i[m]] = m_run[m];
+                sm.row_l[my_i[m]] = l_run[m];
+            }
+        }
+    }
+    wave_lds_fence();
+
+    finish_piece<D, RB, EPL, NAK>(a, sm.row_m, sm.row_l, acc, lane, lrow * NAK, doff, qrow0, row0, R,
+                                  n_rb, b, g, rb, off, L, W, P, p);
+    wave_lds_fence();   // row_m/row_l/pbuf are rewritten by the next piece
+}
+
+template <class FMT, int D, int RB>
+__global__ void __launch_bounds__(kWave)
+decode_valu(const Args a, const int R, const int n_rb)
+{
+    __shared__ ValuShared<FMT, D, RB> sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
+    zero_empty_sequences<D>(a, P, p);
+    const long long W = sched.total;
+    if (W == 0) return;
+    for_each_piece(a, sched, n_rb, P, p,
+                   [&](int b, int g, int rb, int ta, int tb, long long off, int Lb) {
+                       valu_piece<FMT, D, RB>(a, sm, R, n_rb, b, g, rb, ta, tb, off, Lb, W, P, p);
+                   });
+}
+
+// ---------------------------------------------------------------------------
+// bf16, up to 16 query rows per segment: scores on the matrix cores.
+// S[16 query rows x 16 cache rows] = Q . K^T with v_mfma_f32_16x16x32_bf16
+// (D/32 instructions per tile, fp32 accumulation); the softmax and the
+// weighted V sum stay on the vector ALU in fp32.
+//   operand A (Q):   lane l holds query row l % 16, elements 8*(l/16) + 32*kk .. +8
+//   operand B (K^T): lane l holds cache row tile + l % 16, the same elements
+//   result:          lane l holds S[4*(l/16) + jj][l % 16], jj = 0..3
+// A and B give every lane's k slots the same head-dim elements, so the
+// products pair up correctly whatever order the unit sums them in.  Rows of
+// the block past RB (or past R) are zero in A and masked in S.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLensWindow = 256;   // seq_lens entries a wave keeps in LDS
+
+struct MqkShared {
+    float pbuf[16][16];      // p of the current tile: [cache row][query row]
+    float row_m[16];         // per-row max and sum at the end of a piece
+    float row_l[16];
+    int lens[kLensWindow];   // clamped seq_lens[first_b + i]
+};
+
+template <int M>
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, xchg<15>(x));
+    x = fmaxf(x, xchg<7>(x));
+    x = fmaxf(x, xchg<2>(x));
+    x = fmaxf(x, xchg<1>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += xchg<15>(x);
+    x += xchg<7>(x);
+    x += xchg<2>(x);
+    x += xchg<1>(x);
+    return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// One piece: a run [ta, tb) of cache rows of segment (b, g, rb).
+struct Piece {
+    int b, g, rb, ta, tb, L;
+    long long off;       // the segment's first work unit
+};
+
+// Yields this workgroup's pieces in order (the same walk as for_each_piece).
+struct PieceIter {
+    long long A, E, Eb, k;
+    int b, units, n_rb;
+
+    __device__ __forceinline__ void init(const Sched& sh, int G, int n_rb_, int P, int p)
+    {
+        A = wg_start(sh.total, P, p);
+        E = wg_start(sh.total, P, p + 1);
+        Eb = sh.first_e;
+        b = (int)sh.first_b;
+        k = -1;
+        n_rb = n_rb_;
+        units = G * n_rb_;
+    }
+
+    // lens: LDS copy of the clamped seq_lens from first_b on (kLensWindow of
+    // them): the walk runs inside the tile stream, where a global load would
+    // make the wave wait for every tile load in flight.
+    __device__ __forceinline__ bool next(const Args& a, const int* lens, int base, Piece& pc)
+    {
+        while (b < a.B && Eb < E) {
+            const int Lb = (b - base < kLensWindow) ? lens[b - base] : clamp_len(a.seq_lens, b, a.T);
+            if (Lb > 0) {
+                if (k < 0) k = A > Eb ? (A - Eb) / Lb : 0;
+                if (k < units) {
+                    const long long off = Eb + k * Lb;
+                    if (off < E) {
+                        pc.b = b;
+                        pc.g = (int)(k / n_rb);
+                        pc.rb = (int)(k % n_rb);
+                        pc.ta = (int)(A > off ? A - off : 0);
+                        pc.tb = (int)(E - off < Lb ? E - off : Lb);
+                        pc.L = Lb;
+                        pc.off = off;
+                        ++k;
+                        return true;
+                    }
+                }
+            }
+            Eb += (long long)units * Lb;
+            ++b;
+            k = -1;
+        }
+        return false;
+    }
+};
+
+// One piece of segment (b, g, rb): cache rows [ta, tb).  The wave streams
+// 16-row tiles with the loads of the next two tiles in flight, then writes
+// the piece out (or stores its partial, returned in *pd without waiting).
+template <int D, int RB>
+__device__ __forceinline__ bool mqk_piece(const Args& a, MqkShared& sm, int R, int n_rb, const Piece& pc,
+                                          long long W, int P, int p, Pending* pd)
+{
+    constexpr int NK = D / 32;           // matrix-core k steps per tile
+    constexpr int EPL = 8;               // bf16 per 16-byte load (V layout)
+    constexpr int LPT = D / EPL;         // lanes per cache row in the V layout
+    constexpr int TPL = kWave / LPT;     // cache rows per wave-wide V load
+    constexpr int TW = 16;               // cache rows per tile
+    constexpr int NLV = TW / TPL;        // V loads per lane per tile
+    constexpr int NA = RB * EPL;         // V-sum accumulators per lane
+    constexpr int NAK = NA / TPL;        // kept after the row-group sum
+    static_assert(RB >= 4 && RB <= 16 && NA >= TPL, "row block");
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15;           // MFMA column / A row of this lane
+    const int kg = lane >> 4;            // MFMA k group
+    const int lrow = lane / LPT;         // V layout
+    const int doff = (lane % LPT) * EPL;
+    const int ta = pc.ta, tb = pc.tb;
+    const int row0 = pc.rb * RB;
+    const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
+
+    // A operand: query row `col` of the block (zero past RB or R)
+    uint4 qa[NK];
+    {
+        const bool live = col < RB && row0 + col < R;
+        const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live ? col : 0)) * D + 8 * kg) * 2;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            const uint4 v = load16(qp + 64 * s);
+            qa[s] = live ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    int last[4];
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * kg + jj;
+        last[jj] = (r < RB && row0 + r < R) ? pc.L - a.sq + ((row0 + r) % a.sq) : -1;
+        m_run[jj] = -INFINITY;
+        l_run[jj] = 0.0f;
+    }
+    float acc[NA];
+#pragma unroll
+    for (int u = 0; u < NA; ++u) acc[u] = 0.0f;
+
+    const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
+    const char* kbase = static_cast<const char*>(a.k) + (slab + 8 * kg) * 2;
+    const char* vbase = static_cast<const char*>(a.v) + (slab + doff) * 2;
+
+    // rows past the piece's end re-read row tb - 1 (valid; masked / weight 0)
+    auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
+        const int tk = min(t0 + col, tb - 1);
+#pragma unroll
+        for (int s = 0; s < NK; ++s) kk[s] = load16(kbase + ((int64_t)tk * D + 32 * s) * 2);
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int tv = min(t0 + j * TPL + lrow, tb - 1);
+            vv[j] = load16(vbase + (int64_t)tv * D * 2);
+        }
+    };
+
+    auto compute_tile = [&](int t0, const uint4* kk, const uint4* vv) {
+        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[s]),
+                                                         __builtin_bit_cast(bf16x8_t, kk[s]), s4, 0, 0, 0);
+        const int t = t0 + col;
+        float sc[4], m_new[4];
+        bool grew = false;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            sc[jj] = (t < tb && t <= last[jj]) ? s4[jj] * a.scale_log2 : -INFINITY;
+            m_new[jj] = fmaxf(m_run[jj], row16_max<0>(sc[jj]));
+            grew |= m_new[jj] > m_run[jj];
+        }
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+            float al[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                al[jj] = (m_new[jj] > m_run[jj]) ? __builtin_amdgcn_exp2f(m_run[jj] - m_new[jj]) : 1.0f;
+                l_run[jj] *= al[jj];
+                m_run[jj] = m_new[jj];
+            }
+            // row i's factor sits in the lanes of k group i / 4
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const float f = readlane_f(al[i % 4], 16 * (i / 4));
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[i * EPL + e] *= f;
+            }
+        }
+        float pv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            pv[jj] = (sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run[jj]);
+            l_run[jj] += pv[jj];
+        }
+        if (4 * kg < RB)
+            *reinterpret_cast<float4*>(&sm.pbuf[col][4 * kg]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        wave_lds_fence();
+        // weighted V sum, fp32 weights and fp32 accumulation
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const float* prow = sm.pbuf[j * TPL + lrow];
+            float vf[EPL];
+            Bf16::unpack(vv[j], vf);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const float w = prow[i];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[i * EPL + e] = fmaf(w, vf[e], acc[i * EPL + e]);
+            }
+        }
+        wave_lds_fence();   // next tile's p writes stay behind these reads
+    };
+
+    // Three register buffers in rotation; the loads are unconditional (rows
+    // clamped into the piece) so the compiler waits for exactly the oldest
+    // tile instead of draining the prefetches.
+    {
+        uint4 ka[NK], va[NLV], kb[NK], vb[NLV], kc[NK], vc[NLV];
+        int t0 = ta;
+        const int ntile = (tb - ta + TW - 1) / TW;
+        load_tile(t0, ka, va);
+        load_tile(t0 + TW, kb, vb);
+        for (int it = 0; it < ntile; it += 3) {
+            load_tile(t0 + 2 * TW, kc, vc);
+            compute_tile(t0, ka, va);
+            t0 += TW;
+            if (it + 1 >= ntile) break;
+            load_tile(t0 + 2 * TW, ka, va);
+            compute_tile(t0, kb, vb);
+            t0 += TW;
+            if (it + 2 >= ntile) break;
+            load_tile(t0 + 2 * TW, kb, vb);
+            compute_tile(t0, kc, vc);
+            t0 += TW;
+        }
+    }
+
+    // ---- end of the piece ------------------------------------------------------
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) l_run[jj] = row16_sum(l_run[jj]);
+    reduce_scatter<NA, kWave / 2, LPT, false>(acc, lane);
+    if (col == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 4 * kg + jj;
+            if (r < RB) {
+                sm.row_m[r] = m_run[jj];
+                sm.row_l[r] = l_run[jj];
+            }
+        }
+    }
+    wave_lds_fence();
+    const bool left = piece_output<D, RB, EPL, NAK>(a, sm.row_m, sm.row_l, acc, lrow * NAK, doff, qrow0, row0,
+                                                    R, n_rb, pc.b, pc.g, pc.rb, pc.off, pc.L, W, P, p, pd);
+    wave_lds_fence();   // row_m / row_l / pbuf are rewritten by the next piece
+    return left;
+}
+
+// Pieces are streamed one after another.  A piece that left a partial is
+// counted (and, by the last arrival, merged) right away: merging early
+// spreads the merges over the run instead of piling them up at its end.
+template <int D, int RB>
+__global__ void __launch_bounds__(kWave)
+decode_mqk(const Args a, const int R, const int n_rb)
+{
+    constexpr int EPL = 8;
+    constexpr int LPT = D / EPL;
+    constexpr int NAK = RB * EPL / (kWave / LPT);
+    __shared__ MqkShared sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
+    zero_empty_sequences<D>(a, P, p);
+    const long long W = sched.total;
+    if (W == 0) return;
+    const int lbase = (int)sched.first_b;
+    for (int i = lane; i < kLensWindow; i += kWave)
+        sm.lens[i] = lbase + i < a.B ? clamp_len(a.seq_lens, lbase + i, a.T) : 0;
+    wave_lds_fence();
+
+    PieceIter it;
+    it.init(sched, a.G, n_rb, P, p);
+    Piece pc;
+    while (it.next(a, sm.lens, lbase, pc)) {
+        Pending pd;
+        if (mqk_piece<D, RB>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
+            __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
+            arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, (lane / LPT) * NAK, (lane % LPT) * EPL, R, W, P);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
+typedef void (*DecodeFn)(const Args, int, int);
 
 template <class FMT, int D>
-static SplitFn pick_valu(int rb)
+static DecodeFn pick_valu(int rb)
 {
     switch (rb) {
-    case 1: return split_valu<FMT, D, 1>;
-    case 2: return split_valu<FMT, D, 2>;
-    case 4: return split_valu<FMT, D, 4>;
-    case 8: return split_valu<FMT, D, 8>;
-    case 16: return split_valu<FMT, D, 16>;
+    case 1: return decode_valu<FMT, D, 1>;
+    case 2: return decode_valu<FMT, D, 2>;
+    case 4: return decode_valu<FMT, D, 4>;
+    case 8: return decode_valu<FMT, D, 8>;
+    case 16: return decode_valu<FMT, D, 16>;
     default: return nullptr;
     }
 }
 
-hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream, hipEvent_t split_done)
+template <int D>
+static DecodeFn pick_mqk(int rb)
 {
-    if (p.split_grid <= 0) return hipSuccess;
-    SplitFn fn = nullptr;
-    if (p.path == Path::VALU) {
-        if (p.kv_bf16)
-            fn = p.D == 64 ? pick_valu<Bf16, 64>(p.row_block) : pick_valu<Bf16, 128>(p.row_block);
-        else
-            fn = p.D == 64 ? pick_valu<F32, 64>(p.row_block) : pick_valu<F32, 128>(p.row_block);
+    switch (rb) {
+    case 4: return decode_mqk<D, 4>;
+    case 8: return decode_mqk<D, 8>;
+    case 16: return decode_mqk<D, 16>;
+    default: return nullptr;
     }
+}
+
+static DecodeFn pick(const Plan& p)
+{
+    if (p.path == Path::MFMA) {
+        if (!p.kv_bf16) return nullptr;
+        return p.D == 64 ? pick_mqk<64>(p.row_block) : pick_mqk<128>(p.row_block);
+    }
+    if (p.kv_bf16)
+        return p.D == 64 ? pick_valu<Bf16, 64>(p.row_block) : pick_valu<Bf16, 128>(p.row_block);
+    return p.D == 64 ? pick_valu<F32, 64>(p.row_block) : pick_valu<F32, 128>(p.row_block);
+}
+
+int resident_groups_per_cu(const Plan& p)
+{
+    DecodeFn fn = pick(p);
+    if (!fn) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), kWave, 0) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
+}
+
+int cache_rows_per_wave_tile(const Plan& p)
+{
+    if (p.path == Path::MFMA) return 16;
+    const int es = p.kv_bf16 ? 2 : 4;
+    const int lpt = p.D * es / 16;
+    return kSlotsPerLane * (kWave / lpt);
+}
+
+hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
+{
+    if (p.grid <= 0) return hipSuccess;
+    DecodeFn fn = pick(p);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.split_grid), dim3(kSplitWaves * kWave),
-                       p.lds_bytes, stream, a, p.R, p.n_rb, p.chunk, p.max_chunks);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (split_done) {
-        err = hipEventRecord(split_done, stream);
-        if (err != hipSuccess) return err;
-    }
-    if (p.combine_grid > 0) {
-        if (p.D == 64)
-            hipLaunchKernelGGL(merge_chunks<64>, dim3((unsigned)p.combine_grid), dim3(256), 0,
-                               stream, a, p.chunk, p.max_chunks);
-        else
-            hipLaunchKernelGGL(merge_chunks<128>, dim3((unsigned)p.combine_grid), dim3(256), 0,
-                               stream, a, p.chunk, p.max_chunks);
-        err = hipGetLastError();
-    }
-    return err;
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave), 0, stream, a, p.R, p.n_rb);
+    return hipGetLastError();
 }
 
 }  // namespace gqa

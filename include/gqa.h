@@ -41,7 +41,7 @@
  *
  * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
  * (F32, F32, F32) or (BF16, BF16, F32); H % G == 0; any B >= 0, sq >= 1,
- * T >= 1 with T * D < 2^31.
+ * T >= 1 with T * D < 2^31 and B * G * ceil((H/G)*sq / 16) <= 2^18.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -79,34 +79,31 @@ typedef enum {
 
 /* Optional knobs; zero-initialise for defaults. */
 typedef struct {
-    int32_t path;            /* gqa_path_t                                             */
-    int32_t chunk_tokens;    /* cache rows per workgroup; 0 = planner's choice.  Rounded
-                                up to the kernel's tile and clamped to its limits.     */
-    void *split_done_event;  /* NULL, or a hipEvent_t the call records on stream right
-                                after queueing the split kernel and before the merge
-                                kernel (lets a caller time the two kernels apart)     */
-    int32_t reserved[4];     /* must be zero                                           */
+    int32_t path;        /* gqa_path_t                                                 */
+    int32_t workgroups;  /* workgroups of the (single, persistent) kernel; 0 = as many
+                            as the GPU holds at once.  Each takes an equal share of the
+                            cache rows, so any value gives the same result to rounding. */
+    int32_t reserved[6]; /* must be zero                                               */
 } gqa_options_t;
 
 /* What the planner decided for a shape (filled by gqa_plan). */
 typedef struct {
     int32_t path;           /* GQA_PATH_VALU or GQA_PATH_MFMA                          */
-    int32_t chunk_tokens;   /* cache rows per workgroup                                */
-    int32_t max_chunks;     /* ceil(T / chunk_tokens)                                  */
+    int32_t workgroups;     /* workgroups of the kernel                                */
     int32_t rows_per_group; /* (H/G)*sq: query rows sharing one KV head                */
-    int32_t row_blocks;     /* workgroups per (b, KV head, chunk) along the rows       */
-    int32_t split_grid;     /* workgroups of the split kernel                          */
-    int32_t combine_grid;   /* workgroups of the merge kernel (0: not launched)        */
-    int32_t reserved;
+    int32_t row_blocks;     /* segments per (b, KV head) along those rows              */
+    int32_t row_block;      /* query rows per segment                                  */
+    int32_t reserved[3];
     uint64_t workspace_bytes; /* device scratch the call needs                        */
 } gqa_plan_t;
 
 /*
  * gqa_decode -- out = grouped-query attention (see top of file).
- * Uses a workspace owned by the library: one buffer per device, grown on
- * demand (hipMalloc, after waiting for the device) and kept until process
- * exit.  Calls that run concurrently on different streams of one device
- * must use gqa_decode_ws with their own workspaces instead.
+ * One kernel launch.  Uses a workspace owned by the library: one buffer per
+ * device, grown on demand (hipMalloc and a zero fill, after waiting for the
+ * device) and kept until process exit.  Calls that run concurrently on
+ * different streams of one device must use gqa_decode_ws with their own
+ * workspaces instead.
  * scale: any finite float (the pages use 1/sqrt(D)).
  */
 gqa_status_t gqa_decode(const gqa_shape_t *shape, const void *q,
@@ -119,8 +116,13 @@ size_t gqa_workspace_bytes(const gqa_shape_t *shape);
 
 /*
  * gqa_decode_ws -- as gqa_decode, with a caller-owned device workspace of
- * ws_bytes >= gqa_workspace_bytes(shape) bytes (may be NULL when that is 0).
- * The workspace must stay untouched until the queued work finishes.
+ * ws_bytes >= gqa_workspace_bytes(shape) bytes.  The workspace starts with
+ * a fixed 1 MiB region of arrival counters (one per sequence, KV head and
+ * row block) followed by per-workgroup partial results.  It must be
+ * zero-filled once before its first use (for example with hipMemset); every
+ * call leaves the counter region zero again, so the buffer can be reused for
+ * any shape without clearing.  It must not be touched, and must not be
+ * shared with another call, until the queued work finishes.
  */
 gqa_status_t gqa_decode_ws(const gqa_shape_t *shape, const void *q,
                            const void *k_cache, const void *v_cache,
@@ -130,8 +132,8 @@ gqa_status_t gqa_decode_ws(const gqa_shape_t *shape, const void *q,
 /*
  * gqa_decode_ex -- as gqa_decode_ws with tuning options (may be NULL).
  * Results for a given input are deterministic for a given plan; different
- * chunk sizes agree to rounding.  workspace NULL with ws_bytes 0 selects
- * the library-owned workspace of gqa_decode.
+ * workgroup counts agree to rounding.  workspace NULL with ws_bytes 0
+ * selects the library-owned workspace of gqa_decode.
  */
 gqa_status_t gqa_decode_ex(const gqa_shape_t *shape, const void *q,
                            const void *k_cache, const void *v_cache,

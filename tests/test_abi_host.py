@@ -49,33 +49,42 @@ def _shape(**kw):
     return gqa.Shape(**base)
 
 
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_plan_of_batched_gqa8(lib):
     p = gqa.plan(_shape(B=32))
     assert p["rows_per_group"] == 4
-    assert p["row_blocks"] == 1
-    assert p["max_chunks"] * p["chunk_tokens"] >= 4096
-    assert p["split_grid"] == 32 * 8 * p["max_chunks"]
-    # the workspace holds one (D + 1)-float partial per output row and chunk,
-    # far below a repeated K/V copy (n_rep = 4 times the cache)
+    assert p["row_blocks"] == 1 and p["row_block"] == 4
+    P = p["workgroups"]
+    assert 1 <= P <= 4096
+    # workspace: a fixed 1 MiB counter region, then two partial slots per
+    # workgroup (4 query rows x 128 values + 16 lse floats) -- far below a
+    # repeated K/V copy (n_rep = 4 times the cache)
+    assert p["workspace_bytes"] == (1 << 20) + _round256(P * 2 * (4 * 128 + 16) * 4)
     kv_bytes = 2 * 32 * 8 * 4096 * 128 * 2
-    assert p["workspace_bytes"] == 32 * 32 * p["max_chunks"] * 129 * 4
     assert p["workspace_bytes"] < kv_bytes // 50
     assert gqa.workspace_bytes(_shape(B=32)) == p["workspace_bytes"]
 
 
-def test_plan_chunk_option_rounds_to_tile(lib):
-    p = gqa.plan(_shape(), chunk_tokens=100)
-    assert p["chunk_tokens"] % 64 == 0 and p["chunk_tokens"] >= 100
-    p1 = gqa.plan(_shape(T=100), chunk_tokens=0)
-    assert p1["max_chunks"] >= 1
+def test_plan_workgroup_option(lib):
+    p = gqa.plan(_shape(), workgroups=100)
+    assert p["workgroups"] == 100
+    small = gqa.plan(_shape(B=1, T=100))
+    # a tiny cache gets no more workgroups than it has pairs of wave tiles:
+    # 8 KV heads x 100 rows / (2 x 16 rows)
+    assert 1 <= small["workgroups"] <= 25
 
 
 def test_plan_row_blocks_for_large_groups(lib):
     p = gqa.plan(_shape(G=1, sq=2, q_dtype=gqa.GQA_F32, kv_dtype=gqa.GQA_F32), path=gqa.PATH_VALU)
     assert p["rows_per_group"] == 64
-    assert p["row_blocks"] == 4
+    assert p["row_blocks"] == 4 and p["row_block"] == 16
     p = gqa.plan(_shape(H=6, G=1, sq=3), path=gqa.PATH_VALU)
     assert p["rows_per_group"] == 18 and p["row_blocks"] == 2
+    p = gqa.plan(_shape(H=12, G=4, sq=1), path=gqa.PATH_VALU)
+    assert p["rows_per_group"] == 3 and p["row_block"] == 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -89,6 +98,7 @@ def test_plan_row_blocks_for_large_groups(lib):
     (dict(out_dtype=gqa.GQA_BF16), gqa.GQA_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), gqa.GQA_ERR_UNSUPPORTED),
     (dict(T=1 << 25, D=128), gqa.GQA_ERR_INVALID_ARG),
+    (dict(B=1 << 16, G=8, H=32), gqa.GQA_ERR_INVALID_ARG),     # > 2^18 segments
 ])
 def test_bad_shapes_rejected(lib, kw, status):
     s = _shape(**kw)
@@ -142,7 +152,7 @@ def test_bad_options_rejected(lib):
         gqa.plan(s, path=9)
     assert ei.value.status == gqa.GQA_ERR_INVALID_ARG
     with pytest.raises(gqa.GqaError):
-        gqa.plan(s, chunk_tokens=-1)
+        gqa.plan(s, workgroups=-1)
     o = gqa.Options()
     o.reserved[2] = 1
     info = gqa.PlanInfo()

@@ -163,31 +163,40 @@ def test_closed_forms_on_gpu(gqa):
         assert (got[b, :, 0] - want).abs().max().item() <= 1e-5
 
 
-def test_chunking_invariance_and_determinism(gqa, orc):
-    w = gi.WORKLOADS["batched_b32_h32_g8_d128_t4096_ragged"].scaled(B=4, seed=77)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_split_invariance_and_determinism(gqa, orc, dt):
+    """Any number of workgroups (pieces per segment from 1 to dozens) gives
+    the oracle's result; the same plan gives the same bits every call."""
+    w = gi.WORKLOADS["batched_b32_h32_g8_d128_t4096_ragged"].scaled(B=4, seed=77, dtype=dt)
     x = gi.make_inputs(w)
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], threads=8)
     xc = _to(x, "cuda")
     outs = []
-    for ct in (64, 128, 512, 2048):
-        o = _run(gqa, xc, chunk_tokens=ct)
-        _compare(o, want, TOL["bf16"], "chunk %d" % ct)
+    for P in (1, 3, 32, 97, 1000):
+        o = _run(gqa, xc, workgroups=P)
+        _compare(o, want, TOL[dt], "workgroups %d" % P)
         outs.append(o)
     for a in outs[1:]:
-        assert (a - outs[0]).abs().max().item() <= 2e-3
-    again = _run(gqa, xc, chunk_tokens=128)
-    assert torch.equal(again, outs[1])
+        assert (a - outs[0]).abs().max().item() <= TOL[dt]
+    for _ in range(3):
+        again = _run(gqa, xc, workgroups=97)
+        assert torch.equal(again, outs[3])
 
 
 def test_explicit_workspace_matches_library_workspace(gqa):
+    """A caller workspace (zero-filled once) gives the library workspace's
+    bits, and its counters are left zeroed after every call."""
     w = gi.WORKLOADS["batched_b32_h32_g8_d128_t4096_ragged"].scaled(B=8, seed=78)
     xc = gi.make_inputs(w, device="cuda")
     need = gqa.workspace_bytes(gqa.shape_of(xc["q"], xc["k"]))
     assert need > 0
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     a = _run(gqa, xc)
-    b = _run(gqa, xc, workspace=ws)
-    assert torch.equal(a, b)
+    for _ in range(3):
+        b = _run(gqa, xc, workspace=ws)
+        assert torch.equal(a, b)
+    # the counter region (first MiB) is zero again after every call
+    assert int(ws[:1 << 20].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_no_repeated_kv_is_allocated(gqa):
@@ -201,11 +210,12 @@ def test_no_repeated_kv_is_allocated(gqa):
     free0, _ = torch.cuda.mem_get_info()
     out = torch.empty(xc["q"].shape, dtype=torch.float32, device="cuda")
     free1, _ = torch.cuda.mem_get_info()
-    _run(gqa, xc, out=out, chunk_tokens=64)   # a plan with a large workspace
+    _run(gqa, xc, out=out)
     free2, _ = torch.cuda.mem_get_info()
     repeated = 4 * 2 * xc["k"].numel() * xc["k"].element_size()
     taken = free1 - free2
     assert taken <= max(2 * ws, 64 << 20)
+    assert ws < repeated // 100
     assert taken < repeated // 20
     del free0
 
@@ -221,3 +231,17 @@ def test_stream_ordering(gqa, orc):
         out = gqa.decode(xc["q"], xc["k"], xc["v"], xc["seq_lens"])
     s.synchronize()
     _compare(out, want, TOL["bf16"], "side stream")
+
+
+@pytest.mark.parametrize("path_name", ["valu", "mfma"])
+@pytest.mark.parametrize("G,sq", [(8, 1), (4, 2), (2, 1), (32, 2)])
+def test_both_paths_match_oracle(gqa, orc, path_name, G, sq):
+    """bf16 runs on either path: vector-ALU scores or matrix-core scores."""
+    path = {"valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA}[path_name]
+    x = gi.make_custom(3, 32, G, 128, 900, sq, dtype="bf16", seed=40 + G + sq,
+                       seq_lens=[900, 411, 37])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"])
+    got = _run(gqa, _to(x, "cuda"), path=path)
+    _compare(got, want, TOL["bf16"], "%s G=%d sq=%d" % (path_name, G, sq))
+    p = gqa.plan(gqa.shape_of(x["q"], x["k"]), path=path)
+    assert p["path"] == path
