@@ -108,7 +108,7 @@ def cpu_baseline(x_cpu, w, sum_len, seconds: float):
         oracle.decode_f64(q, k, v, sl, scale, threads=threads)
         passes += 1
         el = time.perf_counter() - t0
-        if el >= seconds or passes >= 200:
+        if el >= seconds:
             break
     per = el / passes
     ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
@@ -127,7 +127,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=gi.HEADLINE, choices=sorted(gi.WORKLOADS))
     ap.add_argument("--workgroups", type=int, default=0)
-    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_qk"])
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -160,7 +160,8 @@ def main(argv=None):
     x = gi.make_inputs(w, device=dev)
     sum_len = int(x["seq_lens"].clamp(0, w.T).sum().item())
     ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
-    path = {"auto": gqa.PATH_AUTO, "valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA}[args.path]
+    path = {"auto": gqa.PATH_AUTO, "valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA,
+            "mfma_qk": gqa.PATH_MFMA_QK}[args.path]
     shape = gqa.shape_of(x["q"], x["k"])
     plan = gqa.plan(shape, path=path, workgroups=args.workgroups)
     log("[bench] plan %s" % plan)
@@ -265,7 +266,7 @@ def main(argv=None):
                                      if w.ragged else "all T"),
             "sum_seq_lens": sum_len, "kv_dtype": w.dtype, "out_dtype": "f32",
             "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
-            "path": {1: "valu", 2: "mfma"}.get(plan["path"], "?"),
+            "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
         },
         "us_per_step": round(ms * 1e3, 2),
@@ -281,7 +282,7 @@ def main(argv=None):
         "max_abs_err_vs_oracle_b0": parity,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_valu" if plan["path"] == 1 else "decode_mfma",
+            "kernel": {1: "decode_valu", 2: "decode_mfa", 3: "decode_mqk"}[plan["path"]],
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -20,7 +20,7 @@ import os
 import threading
 
 __all__ = ["decode", "plan", "workspace_bytes", "version", "library_path",
-           "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
+           "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
 GQA_F32, GQA_BF16 = 0, 1
-PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",

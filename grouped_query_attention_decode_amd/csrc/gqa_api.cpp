@@ -84,23 +84,29 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         wg_req = o->workgroups;
         for (int i = 0; i < 6; ++i)
             if (o->reserved[i] != 0) return fail(GQA_ERR_INVALID_ARG, "options.reserved must be zero");
-        if (path_req < GQA_PATH_AUTO || path_req > GQA_PATH_MFMA)
+        if (path_req < GQA_PATH_AUTO || path_req > GQA_PATH_MFMA_QK)
             return fail(GQA_ERR_INVALID_ARG, "unknown path %d", path_req);
         if (wg_req < 0) return fail(GQA_ERR_INVALID_ARG, "workgroups must be >= 0");
     }
-    if (path_req == GQA_PATH_MFMA && !bf16)
-        return fail(GQA_ERR_UNSUPPORTED, "the MFMA path needs bf16 q/k/v");
+    if ((path_req == GQA_PATH_MFMA || path_req == GQA_PATH_MFMA_QK) && !bf16)
+        return fail(GQA_ERR_UNSUPPORTED, "the matrix-core paths need bf16 q/k/v");
 
     const int R = (int)R64;
-    // bf16 scores go to the matrix cores; fp32 (or a forced VALU path) stays
-    // on the vector ALU
+    // bf16 goes to the matrix cores (both products unless asked otherwise);
+    // fp32, or a forced VALU path, stays on the vector ALU
     const bool mfma = bf16 && path_req != GQA_PATH_VALU;
-    p->path = mfma ? gqa::Path::MFMA : gqa::Path::VALU;
+    if (!mfma)
+        p->path = gqa::Path::VALU;
+    else if (path_req == GQA_PATH_MFMA_QK)
+        p->path = gqa::Path::MFMA_QK;
+    else
+        p->path = gqa::Path::MFMA;
     p->kv_bf16 = bf16 ? 1 : 0;
     p->D = s->D;
     p->R = R;
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
-    if (mfma && p->row_block < 4) p->row_block = 4;   // one k group of the 16x16 tile
+    if (p->path == gqa::Path::MFMA_QK && p->row_block < 4) p->row_block = 4;   // one k group of the 16x16 tile
+    if (p->path == gqa::Path::MFMA) p->row_block = 16;   // the query rows of one 16x16 tile
     p->n_rb = (R + p->row_block - 1) / p->row_block;
     if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
         return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
@@ -259,7 +265,8 @@ gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_p
     gqa_status_t st = make_plan(shape, opts, &p);
     if (st != GQA_OK) return st;
     std::memset(plan, 0, sizeof(*plan));
-    plan->path = p.path == gqa::Path::MFMA ? GQA_PATH_MFMA : GQA_PATH_VALU;
+    plan->path = p.path == gqa::Path::MFMA ? GQA_PATH_MFMA
+                 : p.path == gqa::Path::MFMA_QK ? GQA_PATH_MFMA_QK : GQA_PATH_VALU;
     plan->workgroups = (int32_t)p.grid;
     plan->rows_per_group = p.R;
     plan->row_blocks = p.n_rb;

@@ -18,14 +18,14 @@ constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (meas
 // partials; the partials follow.
 constexpr size_t kCounterRegion = (size_t)kMaxSegments * sizeof(int32_t);
 
-enum class Path : int { VALU = 1, MFMA = 2 };
+enum class Path : int { VALU = 1, MFMA = 2, MFMA_QK = 3 };
 
 struct Plan {
     Path path;
     int kv_bf16;        // 1: bf16 q/k/v, 0: fp32
     int D;
     int R;              // (H/G)*sq query rows per KV head
-    int row_block;      // rows per segment (VALU: power of two <= 16)
+    int row_block;      // rows per segment (power of two <= 16; 16 on the MFMA path)
     int n_rb;           // row blocks per (b, g)
     int64_t grid;       // workgroups (one wave each) P
     size_t part_bytes;  // partials: P * 2 * (row_block * D + 16) floats

@@ -1130,6 +1130,320 @@ decode_mqk(const Args a, const int R, const int n_rb)
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core pass: both products on the MFMA units (bf16 inputs).
+//
+// Per 16-row tile of cache rows t and the (up to) 16 query rows r of a
+// segment:
+//   S^T[t][r]  = K[t][:] . Q[r][:]           v_mfma_f32_16x16x32_bf16, A = K, B = Q^T
+//   O^T[d][r] += V^T[d][t] . P^T[t][r]        v_mfma_f32_16x16x16_bf16, A = V^T, B = P^T
+// The score accumulator gives lane l the scores of query row l % 16 at cache
+// rows 4 (l / 16) + 0..3 of the tile, which is exactly the B operand the V
+// product wants: the softmax weights never move between lanes.  V^T is read
+// back from LDS (the tile is stored row-major; each lane gathers four rows of
+// one column).  Every output element of lane l belongs to query row l % 16,
+// so a rescale multiplies a lane's accumulators by one factor.
+//
+// The weights p (fp32, in (0, 2^kSlack]) enter the V product as two bf16
+// terms, p = hi + lo, which keeps about 16 bits of each weight; V is exact in
+// bf16, and accumulation is fp32.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The running max is moved only when a tile's max exceeds it by more than
+// kSlack (base-2 units); weights then stay below 2^kSlack.  The result is
+// the same -- numerator and denominator share the reference -- and most
+// tiles skip the rescale.
+constexpr float kSlack = 8.0f;
+
+template <int D>
+struct MfaShared {
+    static constexpr int SE = D + 16;   // LDS row stride (bf16): the four row groups of a read hit distinct banks
+    alignas(16) uint16_t vt[16 * SE];   // V tile, row-major
+    int lens[kLensWindow];              // clamped seq_lens[first_b + i]
+};
+
+// Two floats to packed bf16 (round to nearest even), element 0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1)
+{
+    const f32x2_t v = {x0, x1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950
+// row-swap permutes (VALU only).  The two results of a swap of x with itself
+// hold, in every lane, its own value and its partner's, so combining them
+// gives the pair's result in both lanes, in the same order.
+__device__ __forceinline__ float max_x16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_x32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_x16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float sum_x32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One piece of segment (b, g, rb) -- cache rows [ta, tb) for query rows
+// 16 rb .. 16 rb + 15 -- streamed in 16-row tiles with the next two tiles'
+// loads in flight; then written out, or left as a partial (returned in *pd,
+// stores issued, nothing waited for).
+template <int D>
+__device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
+                                          long long W, int P, int p, Pending* pd)
+{
+    constexpr int NK = D / 32;           // k steps of the score product
+    constexpr int NC = D / 16;           // column blocks of the V product
+    constexpr int SE = MfaShared<D>::SE;
+    constexpr int CPR = D / 8;           // 16-byte chunks per cache row
+    constexpr int NLV = 16 * CPR / kWave;   // V loads per lane per tile
+    constexpr int RB = 16;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15;           // query row of this lane (score / output column)
+    const int kg = lane >> 4;            // k group: cache rows 4 kg .. 4 kg + 3 of a tile
+    const int ta = pc.ta, tb = pc.tb;
+    const int row0 = pc.rb * RB;
+    const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
+    const bool live = row0 + col < R;
+
+    // B operand of the score product: query row `col`, zero past R
+    uint4 qb[NK];
+    {
+        const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live ? col : 0)) * D + 8 * kg) * 2;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            const uint4 v = load16(qp + 64 * s);
+            qb[s] = live ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    const int last = live ? pc.L - a.sq + ((row0 + col) % a.sq) : -1;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4_t acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
+    const char* kbase = static_cast<const char*>(a.k) + (slab + 8 * kg) * 2;
+    const char* vbase = static_cast<const char*>(a.v) + slab * 2;
+
+    // Rows past the piece's end re-read row tb - 1 (valid): their weights
+    // are exactly 0, so no row at or beyond tb is read and no branch guards
+    // the loads.  K: lane (kg, col) loads row col, elements 8 kg + 32 s ..;
+    // V: chunk c = lane + 64 j is row c / CPR, elements 8 (c % CPR) ..
+    auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
+        const int tk = min(t0 + col, tb - 1);
+#pragma unroll
+        for (int s = 0; s < NK; ++s) kk[s] = load16(kbase + ((int64_t)tk * D + 32 * s) * 2);
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int c = lane + kWave * j;
+            const int tv = min(t0 + c / CPR, tb - 1);
+            vv[j] = load16(vbase + ((int64_t)tv * D + (c % CPR) * 8) * 2);
+        }
+    };
+
+    auto compute_tile = [&](int t0, const uint4* kk, const uint4* vv) {
+#pragma unroll
+        for (int j = 0; j < NLV; ++j) {
+            const int c = lane + kWave * j;
+            *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+        }
+        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                         __builtin_bit_cast(bf16x8_t, qb[s]), s4, 0, 0, 0);
+        float sc[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0 + 4 * kg + jj;
+            sc[jj] = (t < tb && t <= last) ? s4[jj] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[jj]);
+        }
+        mx = max_x32(max_x16(mx));
+        // the four lanes of a query row take the same decision
+        const bool need = mx > m_run + kSlack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float al = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+            m_run = need ? mx : m_run;
+            l_run *= al;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] *= al;
+        }
+        float pv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            pv[jj] = (sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run);
+            l_run += pv[jj];
+        }
+        // p = hi + lo, both bf16
+        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
+        const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
+        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
+        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
+        const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
+        const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+        const uint16_t* vr = sm.vt + 4 * kg * SE + col;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const s16x4_t va = {(short)vr[16 * c], (short)vr[SE + 16 * c], (short)vr[2 * SE + 16 * c],
+                                (short)vr[3 * SE + 16 * c]};
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[c], 0, 0, 0);
+        }
+    };
+
+    {
+        uint4 ka[NK], va[NLV], kb[NK], vb[NLV], kc[NK], vc[NLV];
+        int t0 = ta;
+        const int ntile = (tb - ta + 15) / 16;
+        load_tile(t0, ka, va);
+        load_tile(t0 + 16, kb, vb);
+        for (int it = 0; it < ntile; it += 3) {
+            load_tile(t0 + 32, kc, vc);
+            compute_tile(t0, ka, va);
+            t0 += 16;
+            if (it + 1 >= ntile) break;
+            load_tile(t0 + 32, ka, va);
+            compute_tile(t0, kb, vb);
+            t0 += 16;
+            if (it + 2 >= ntile) break;
+            load_tile(t0 + 32, kb, vb);
+            compute_tile(t0, kc, vc);
+            t0 += 16;
+        }
+    }
+
+    // ---- end of the piece ------------------------------------------------------
+    const float l = sum_x32(sum_x16(l_run));
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int p_first = wg_of(pc.off, W, P);
+    const int npieces = wg_of(pc.off + pc.L - 1, W, P) - p_first + 1;
+    if (npieces == 1) {
+        if (live) {
+            float* o = a.out + (qrow0 + col) * D + 4 * kg;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[c] * inv;
+        }
+        return false;
+    }
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int mine = slot_base<D, RB>(p, pc.off, W, P);
+    if (live) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const f32x4_t o = acc[c] * inv;
+            const float ov[4] = {o[0], o[1], o[2], o[3]};
+            store4_coherent(part, mine + col * D + 16 * c + 4 * kg, ov);
+        }
+        if (kg == 0) store_coherent(part, mine + RB * D + col, l > 0.0f ? m_run + __log2f(l) : -INFINITY);
+    }
+    pd->seg = (pc.b * a.G + pc.g) * n_rb + pc.rb;
+    pd->p_first = p_first;
+    pd->npieces = npieces;
+    pd->off = pc.off;
+    pd->qrow0 = qrow0;
+    pd->row0 = row0;
+    return true;
+}
+
+// Merge of a segment's partials by its last arrival (slots of RB rows of D
+// values, then the rows' log2-sum-exp).  Lane work item u = lane + 64 i is
+// row u / (D / 4), elements 4 (u % (D / 4)) ..; pieces are taken in order,
+// eight at a time with all their loads in flight.
+template <int D, int RB>
+__device__ __forceinline__ void merge_rows(const Args& a, const Pending& pd, int lane, int R, long long W, int P)
+{
+    constexpr int Q4 = D / 4;
+    constexpr int KB = 8;
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != pd.npieces - 1) return;
+
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int rows = min(RB, R - pd.row0);
+    for (int u = lane; u < rows * Q4; u += kWave) {
+        const int i = u / Q4;
+        const int e = 4 * (u % Q4);
+        float M = -INFINITY, den = 0.0f;
+        float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k0 = 0; k0 < pd.npieces; k0 += KB) {
+            float lse[KB], ov[KB][4];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int base = slot_base<D, RB>(pd.p_first + min(k0 + kk, pd.npieces - 1), pd.off, W, P);
+                lse[kk] = load_coherent(part, base + RB * D + i);
+                load4_coherent(part, base + i * D + e, ov[kk]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                if (k0 + kk >= pd.npieces) break;
+                const float x = lse[kk];
+                if (x == -INFINITY) continue;
+                const float Mn = fmaxf(M, x);
+                const float sc = __builtin_amdgcn_exp2f(M - Mn);
+                const float w = __builtin_amdgcn_exp2f(x - Mn);
+                den = fmaf(den, sc, w);
+                M = Mn;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) num[q] = fmaf(num[q], sc, w * ov[kk][q]);
+            }
+        }
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        float* o = a.out + (pd.qrow0 + i) * D + e;
+        *reinterpret_cast<float4*>(o) = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+    }
+    if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWave)
+decode_mfa(const Args a, const int R, const int n_rb)
+{
+    __shared__ MfaShared<D> sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
+    zero_empty_sequences<D>(a, P, p);
+    const long long W = sched.total;
+    if (W == 0) return;
+    const int lbase = (int)sched.first_b;
+    for (int i = lane; i < kLensWindow; i += kWave)
+        sm.lens[i] = lbase + i < a.B ? clamp_len(a.seq_lens, lbase + i, a.T) : 0;
+    wave_lds_fence();
+
+    PieceIter it;
+    it.init(sched, a.G, n_rb, P, p);
+    Piece pc;
+    while (it.next(a, sm.lens, lbase, pc)) {
+        Pending pd;
+        if (mfa_piece<D>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
+            __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
+            merge_rows<D, 16>(a, pd, lane, R, W, P);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch
 // ---------------------------------------------------------------------------
 typedef void (*DecodeFn)(const Args, int, int);
@@ -1161,6 +1475,10 @@ static DecodeFn pick_mqk(int rb)
 static DecodeFn pick(const Plan& p)
 {
     if (p.path == Path::MFMA) {
+        if (!p.kv_bf16 || p.row_block != 16) return nullptr;
+        return p.D == 64 ? decode_mfa<64> : decode_mfa<128>;
+    }
+    if (p.path == Path::MFMA_QK) {
         if (!p.kv_bf16) return nullptr;
         return p.D == 64 ? pick_mqk<64>(p.row_block) : pick_mqk<128>(p.row_block);
     }
@@ -1184,7 +1502,7 @@ int resident_groups_per_cu(const Plan& p)
 
 int cache_rows_per_wave_tile(const Plan& p)
 {
-    if (p.path == Path::MFMA) return 16;
+    if (p.path != Path::VALU) return 16;
     const int es = p.kv_bf16 ? 2 : 4;
     const int lpt = p.D * es / 16;
     return kSlotsPerLane * (kWave / lpt);

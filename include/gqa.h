@@ -72,9 +72,12 @@ typedef struct {
 
 /* Kernel choice for the split pass. */
 typedef enum {
-    GQA_PATH_AUTO = 0, /* MFMA when (H/G)*sq >= 16 and inputs are bf16, else VALU */
-    GQA_PATH_VALU = 1, /* vector ALU dot products, any supported shape             */
-    GQA_PATH_MFMA = 2  /* bf16 matrix cores; bf16 inputs only                      */
+    GQA_PATH_AUTO = 0,    /* bf16 inputs: a matrix-core path; fp32: VALU              */
+    GQA_PATH_VALU = 1,    /* vector ALU dot products, any supported shape             */
+    GQA_PATH_MFMA = 2,    /* bf16 matrix cores for both products (scores, V sum);
+                             bf16 inputs only                                         */
+    GQA_PATH_MFMA_QK = 3  /* bf16 matrix cores for the scores, vector ALU for the
+                             V sum; bf16 inputs only                                  */
 } gqa_path_t;
 
 /* Optional knobs; zero-initialise for defaults. */
@@ -88,7 +91,7 @@ typedef struct {
 
 /* What the planner decided for a shape (filled by gqa_plan). */
 typedef struct {
-    int32_t path;           /* GQA_PATH_VALU or GQA_PATH_MFMA                          */
+    int32_t path;           /* GQA_PATH_VALU, GQA_PATH_MFMA or GQA_PATH_MFMA_QK        */
     int32_t workgroups;     /* workgroups of the kernel                                */
     int32_t rows_per_group; /* (H/G)*sq: query rows sharing one KV head                */
     int32_t row_blocks;     /* segments per (b, KV head) along those rows              */

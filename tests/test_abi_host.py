@@ -55,17 +55,22 @@ def _round256(x):
 
 def test_plan_of_batched_gqa8(lib):
     p = gqa.plan(_shape(B=32))
+    assert p["path"] == gqa.PATH_MFMA
     assert p["rows_per_group"] == 4
-    assert p["row_blocks"] == 1 and p["row_block"] == 4
+    # the matrix-core path works on 16-row query blocks (4 rows live)
+    assert p["row_blocks"] == 1 and p["row_block"] == 16
     P = p["workgroups"]
     assert 1 <= P <= 4096
     # workspace: a fixed 1 MiB counter region, then two partial slots per
-    # workgroup (4 query rows x 128 values + 16 lse floats) -- far below a
+    # workgroup (16 query rows x 128 values + 16 lse floats) -- far below a
     # repeated K/V copy (n_rep = 4 times the cache)
-    assert p["workspace_bytes"] == (1 << 20) + _round256(P * 2 * (4 * 128 + 16) * 4)
+    assert p["workspace_bytes"] == (1 << 20) + _round256(P * 2 * (16 * 128 + 16) * 4)
     kv_bytes = 2 * 32 * 8 * 4096 * 128 * 2
-    assert p["workspace_bytes"] < kv_bytes // 50
+    assert p["workspace_bytes"] < kv_bytes // 20
     assert gqa.workspace_bytes(_shape(B=32)) == p["workspace_bytes"]
+    q = gqa.plan(_shape(B=32), path=gqa.PATH_MFMA_QK)
+    assert q["path"] == gqa.PATH_MFMA_QK and q["row_block"] == 4
+    assert q["workspace_bytes"] == (1 << 20) + _round256(q["workgroups"] * 2 * (4 * 128 + 16) * 4)
 
 
 def test_plan_workgroup_option(lib):

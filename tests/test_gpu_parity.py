@@ -123,6 +123,18 @@ def test_edge_shapes(gqa, orc, case):
     _compare(got, want, TOL[dt], str(case))
 
 
+@pytest.mark.parametrize("case", [c for c in EDGE if c[6] == "bf16"],
+                         ids=lambda c: "B%d_H%d_G%d_D%d_T%d_sq%d_%s" % c[:7])
+@pytest.mark.parametrize("path_name", ["mfma", "mfma_qk"])
+def test_edge_shapes_each_matrix_path(gqa, orc, case, path_name):
+    B, H, G, D, T, sq, dt, lens = case
+    path = {"mfma": gqa.PATH_MFMA, "mfma_qk": gqa.PATH_MFMA_QK}[path_name]
+    x = gi.make_custom(B, H, G, D, T, sq, dtype=dt, seed=200 + T, seq_lens=lens)
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
+    got = _run(gqa, _to(x, "cuda"), path=path)
+    _compare(got, want, TOL[dt], "%s %s" % (path_name, case))
+
+
 def test_null_seq_lens_means_full_cache(gqa, orc):
     x = gi.make_custom(2, 32, 8, 128, 500, 1, dtype="bf16", seed=5)
     want = orc.decode_f64(x["q"], x["k"], x["v"], None)
@@ -132,16 +144,18 @@ def test_null_seq_lens_means_full_cache(gqa, orc):
     _compare(got, want, TOL["bf16"], "seq_lens=None")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_poisoned_tail_is_never_read(gqa, dt):
+@pytest.mark.parametrize("dt,path_name", [("bf16", "auto"), ("bf16", "mfma"), ("bf16", "mfma_qk"),
+                                          ("f32", "auto")])
+def test_poisoned_tail_is_never_read(gqa, dt, path_name):
     """Cache rows at or beyond seq_lens hold NaN; the output must be finite
     and bit-identical to the run with ordinary values there."""
     args = (3, 32, 8, 128, 700, 2)
     lens = [700, 333, 5]
+    path = {"auto": gqa.PATH_AUTO, "mfma": gqa.PATH_MFMA, "mfma_qk": gqa.PATH_MFMA_QK}[path_name]
     clean = _to(gi.make_custom(*args, dtype=dt, seed=9, seq_lens=lens), "cuda")
     dirty = _to(gi.make_custom(*args, dtype=dt, seed=9, seq_lens=lens, poison_tail=True), "cuda")
-    a = _run(gqa, clean)
-    b = _run(gqa, dirty)
+    a = _run(gqa, clean, path=path)
+    b = _run(gqa, dirty, path=path)
     assert torch.isfinite(b).all()
     assert torch.equal(a, b)
 
@@ -163,23 +177,24 @@ def test_closed_forms_on_gpu(gqa):
         assert (got[b, :, 0] - want).abs().max().item() <= 1e-5
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_split_invariance_and_determinism(gqa, orc, dt):
+@pytest.mark.parametrize("dt,path_name", [("bf16", "mfma"), ("bf16", "mfma_qk"), ("f32", "auto")])
+def test_split_invariance_and_determinism(gqa, orc, dt, path_name):
     """Any number of workgroups (pieces per segment from 1 to dozens) gives
     the oracle's result; the same plan gives the same bits every call."""
+    path = {"auto": gqa.PATH_AUTO, "mfma": gqa.PATH_MFMA, "mfma_qk": gqa.PATH_MFMA_QK}[path_name]
     w = gi.WORKLOADS["batched_b32_h32_g8_d128_t4096_ragged"].scaled(B=4, seed=77, dtype=dt)
     x = gi.make_inputs(w)
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], threads=8)
     xc = _to(x, "cuda")
     outs = []
     for P in (1, 3, 32, 97, 1000):
-        o = _run(gqa, xc, workgroups=P)
+        o = _run(gqa, xc, workgroups=P, path=path)
         _compare(o, want, TOL[dt], "workgroups %d" % P)
         outs.append(o)
     for a in outs[1:]:
         assert (a - outs[0]).abs().max().item() <= TOL[dt]
     for _ in range(3):
-        again = _run(gqa, xc, workgroups=97)
+        again = _run(gqa, xc, workgroups=97, path=path)
         assert torch.equal(again, outs[3])
 
 
@@ -233,11 +248,11 @@ def test_stream_ordering(gqa, orc):
     _compare(out, want, TOL["bf16"], "side stream")
 
 
-@pytest.mark.parametrize("path_name", ["valu", "mfma"])
+@pytest.mark.parametrize("path_name", ["valu", "mfma", "mfma_qk"])
 @pytest.mark.parametrize("G,sq", [(8, 1), (4, 2), (2, 1), (32, 2)])
 def test_both_paths_match_oracle(gqa, orc, path_name, G, sq):
     """bf16 runs on either path: vector-ALU scores or matrix-core scores."""
-    path = {"valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA}[path_name]
+    path = {"valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA, "mfma_qk": gqa.PATH_MFMA_QK}[path_name]
     x = gi.make_custom(3, 32, G, 128, 900, sq, dtype="bf16", seed=40 + G + sq,
                        seq_lens=[900, 411, 37])
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"])
