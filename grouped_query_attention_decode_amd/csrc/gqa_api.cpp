@@ -125,6 +125,10 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     int64_t P = (int64_t)device_compute_units() * occ;
     const int64_t by_size = (max_units + min_share - 1) / min_share;
     if (P > by_size) P = by_size;
+    // A split segment is merged by one wave reading every piece's partial:
+    // keep the pieces per segment (at full length) bounded.
+    const int64_t by_merge = (int64_t)s->B * s->G * p->n_rb * gqa::kMaxPiecesPerSegment;
+    if (P > by_merge) P = by_merge;
     if (wg_req > 0) P = wg_req;
     if (P > (1 << 20)) P = 1 << 20;
     if (P < 1) P = 1;

@@ -13,6 +13,7 @@ constexpr int kSlotsPerLane = 4;   // cache rows one lane loads per tile (VALU)
 constexpr int kMaxRowBlock = 16;   // query rows per VALU segment
 constexpr int kMaxSegments = 1 << 18;  // (sequence, KV head, row block) triples per call
 constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (measured best)
+constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
 // The workspace starts with one arrival counter per possible segment, at a
 // fixed place whatever the shape, so counters never land on another call's
 // partials; the partials follow.

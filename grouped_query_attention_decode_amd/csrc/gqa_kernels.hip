@@ -195,6 +195,15 @@ __device__ __forceinline__ uint4 load16(const char* p)
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// Streaming (non-temporal) 16-byte load, for K/V rows read once per call:
+// they are not kept in the caches at the expense of other lines.
+__device__ __forceinline__ uint4 load16_stream(const char* p)
+{
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int T)
 {
     int L = seq_lens ? seq_lens[b] : T;
@@ -388,6 +397,28 @@ __device__ __forceinline__ int slot_base(int q, long long off, long long W, int 
     return (q * 2 + (wg_start(W, P, q) >= off ? 0 : 1)) * (RB * D + 16);
 }
 
+// The same for the pieces of one segment, q = p_first + k: only the first
+// workgroup can hold the segment in its second slot (tail1: it started
+// before the segment), so no division per piece.
+template <int D, int RB>
+__device__ __forceinline__ int piece_slot(int p_first, int k, bool tail1)
+{
+    return ((p_first + k) * 2 + (k == 0 && tail1 ? 1 : 0)) * (RB * D + 16);
+}
+
+// One step of the running log-sum-exp merge, branch-free (so that the
+// compiler keeps every load of a batch ahead of the arithmetic): x is the
+// piece's log2-sum-exp (-inf for an empty or absent piece); returns the
+// factor for the old sums and sets *w to the piece's weight.
+__device__ __forceinline__ float lse_step(float& M, float x, float* w)
+{
+    const float Mn = fmaxf(M, x);
+    const float sc = (Mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    *w = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - Mn);
+    M = Mn;
+    return sc;
+}
+
 // End of a piece, for one wave.  row_m / row_l (LDS) hold each row's max and
 // sum over the piece; acc[m] is the weighted V sum of query row u / EPL,
 // element doff + u % EPL, for u = ubase + m.  Writes out directly when the
@@ -478,12 +509,13 @@ __device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& p
     }
 #pragma unroll
     for (int m = 0; m < NAK; ++m) num[m] = 0.0f;
+    const bool tail1 = wg_start(W, P, pd.p_first) < pd.off;
     for (int k0 = 0; k0 < pd.npieces; k0 += 4) {
         // the loads of four pieces are in flight together
         float lse[4][NR], ov[4][NAK];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int base = slot_base<D, RB>(pd.p_first + min(k0 + kk, pd.npieces - 1), pd.off, W, P);
+            const int base = piece_slot<D, RB>(pd.p_first, min(k0 + kk, pd.npieces - 1), tail1);
 #pragma unroll
             for (int r = 0; r < NR; ++r) lse[kk][r] = load_coherent(part, base + RB * D + i0 + r);
             if constexpr (NAK % 4 == 0 && EPL % 4 == 0) {
@@ -502,17 +534,12 @@ __device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& p
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            if (k0 + kk >= pd.npieces) break;
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 // running log-sum-exp merge, in piece order
-                const float x = lse[kk][r];
-                if (x == -INFINITY) continue;
-                const float Mn = fmaxf(M[r], x);
-                const float sc = __builtin_amdgcn_exp2f(M[r] - Mn);
-                const float w = __builtin_amdgcn_exp2f(x - Mn);
+                float w;
+                const float sc = lse_step(M[r], k0 + kk < pd.npieces ? lse[kk][r] : -INFINITY, &w);
                 den[r] = fmaf(den[r], sc, w);
-                M[r] = Mn;
 #pragma unroll
                 for (int m = 0; m < NAK; ++m)
                     if ((ubase + m) / EPL == i0 + r) num[m] = fmaf(num[m], sc, w * ov[kk][m]);
@@ -1156,6 +1183,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // tiles skip the rescale.
 constexpr float kSlack = 8.0f;
 
+constexpr int kMfaBuffers = 3;   // tiles held in registers per wave (measured best)
+
 template <int D>
 struct MfaShared {
     static constexpr int SE = D + 16;   // LDS row stride (bf16): the four row groups of a read hit distinct banks
@@ -1248,12 +1277,12 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
         const int tk = min(t0 + col, tb - 1);
 #pragma unroll
-        for (int s = 0; s < NK; ++s) kk[s] = load16(kbase + ((int64_t)tk * D + 32 * s) * 2);
+        for (int s = 0; s < NK; ++s) kk[s] = load16_stream(kbase + ((int64_t)tk * D + 32 * s) * 2);
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
             const int tv = min(t0 + c / CPR, tb - 1);
-            vv[j] = load16(vbase + ((int64_t)tv * D + (c % CPR) * 8) * 2);
+            vv[j] = load16_stream(vbase + ((int64_t)tv * D + (c % CPR) * 8) * 2);
         }
     };
 
@@ -1309,24 +1338,24 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         }
     };
 
+    // NBUF register buffers in rotation, NBUF - 1 tiles' loads in flight
+    // while one is computed.  The loads are unconditional (rows clamped into
+    // the piece), so the compiler waits for exactly the oldest tile.
     {
-        uint4 ka[NK], va[NLV], kb[NK], vb[NLV], kc[NK], vc[NLV];
+        uint4 kb[kMfaBuffers][NK], vb[kMfaBuffers][NLV];
         int t0 = ta;
         const int ntile = (tb - ta + 15) / 16;
-        load_tile(t0, ka, va);
-        load_tile(t0 + 16, kb, vb);
-        for (int it = 0; it < ntile; it += 3) {
-            load_tile(t0 + 32, kc, vc);
-            compute_tile(t0, ka, va);
-            t0 += 16;
-            if (it + 1 >= ntile) break;
-            load_tile(t0 + 32, ka, va);
-            compute_tile(t0, kb, vb);
-            t0 += 16;
-            if (it + 2 >= ntile) break;
-            load_tile(t0 + 32, kb, vb);
-            compute_tile(t0, kc, vc);
-            t0 += 16;
+#pragma unroll
+        for (int u = 0; u < kMfaBuffers - 1; ++u) load_tile(t0 + 16 * u, kb[u], vb[u]);
+        for (int it = 0; it < ntile; it += kMfaBuffers) {
+#pragma unroll
+            for (int u = 0; u < kMfaBuffers; ++u) {
+                if (it + u >= ntile) break;
+                const int nxt = (u + kMfaBuffers - 1) % kMfaBuffers;
+                load_tile(t0 + 16 * (kMfaBuffers - 1), kb[nxt], vb[nxt]);
+                compute_tile(t0, kb[u], vb[u]);
+                t0 += 16;
+            }
         }
     }
 
@@ -1364,53 +1393,77 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 }
 
 // Merge of a segment's partials by its last arrival (slots of RB rows of D
-// values, then the rows' log2-sum-exp).  Lane work item u = lane + 64 i is
-// row u / (D / 4), elements 4 (u % (D / 4)) ..; pieces are taken in order,
-// eight at a time with all their loads in flight.
-template <int D, int RB>
-__device__ __forceinline__ void merge_rows(const Args& a, const Pending& pd, int lane, int R, long long W, int P)
+// values, then the rows' log2-sum-exp), in piece order.  The live rows are
+// spread over the wave, LPR lanes per row, NF float4 of the row per lane;
+// KB pieces are loaded at a time, all their loads in flight together.
+template <int D, int RB, int NF, int KB>
+__device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, int lane, int rows, long long W,
+                                             int P)
 {
-    constexpr int Q4 = D / 4;
-    constexpr int KB = 8;
+    constexpr int LPR = D / (4 * NF);
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int i = lane / LPR;
+    const int ic = min(i, rows - 1);
+    const int e0 = (lane % LPR) * 4 * NF;
+    float M = -INFINITY, den = 0.0f;
+    float num[NF][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) num[f][q] = 0.0f;
+    const bool tail1 = wg_start(W, P, pd.p_first) < pd.off;
+    for (int k0 = 0; k0 < pd.npieces; k0 += KB) {
+        float lse[KB], ov[KB][NF][4];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int base = piece_slot<D, RB>(pd.p_first, min(k0 + kk, pd.npieces - 1), tail1);
+            lse[kk] = load_coherent(part, base + RB * D + ic);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) load4_coherent(part, base + ic * D + e0 + 4 * f, ov[kk][f]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            float w;
+            const float sc = lse_step(M, k0 + kk < pd.npieces ? lse[kk] : -INFINITY, &w);
+            den = fmaf(den, sc, w);
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) num[f][q] = fmaf(num[f][q], sc, w * ov[kk][f][q]);
+        }
+    }
+    if (i < rows) {
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        float* o = a.out + (pd.qrow0 + i) * D + e0;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            *reinterpret_cast<float4*>(o + 4 * f) =
+                make_float4(num[f][0] * inv, num[f][1] * inv, num[f][2] * inv, num[f][3] * inv);
+    }
+}
+
+// Count this wave's arrival for a pending segment of RB = 16 rows; the last
+// arrival merges (choosing the lane layout by the number of live rows) and
+// resets the counter.  The caller has waited for its own partial stores.
+template <int D>
+__device__ __forceinline__ void arrive_and_merge16(const Args& a, const Pending& pd, int lane, int R, long long W,
+                                                   int P)
+{
     int old = 0;
     if (lane == 0)
         old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
     if (old != pd.npieces - 1) return;
-
-    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
-    const int rows = min(RB, R - pd.row0);
-    for (int u = lane; u < rows * Q4; u += kWave) {
-        const int i = u / Q4;
-        const int e = 4 * (u % Q4);
-        float M = -INFINITY, den = 0.0f;
-        float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k0 = 0; k0 < pd.npieces; k0 += KB) {
-            float lse[KB], ov[KB][4];
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-                const int base = slot_base<D, RB>(pd.p_first + min(k0 + kk, pd.npieces - 1), pd.off, W, P);
-                lse[kk] = load_coherent(part, base + RB * D + i);
-                load4_coherent(part, base + i * D + e, ov[kk]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-                if (k0 + kk >= pd.npieces) break;
-                const float x = lse[kk];
-                if (x == -INFINITY) continue;
-                const float Mn = fmaxf(M, x);
-                const float sc = __builtin_amdgcn_exp2f(M - Mn);
-                const float w = __builtin_amdgcn_exp2f(x - Mn);
-                den = fmaf(den, sc, w);
-                M = Mn;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) num[q] = fmaf(num[q], sc, w * ov[kk][q]);
-            }
-        }
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        float* o = a.out + (pd.qrow0 + i) * D + e;
-        *reinterpret_cast<float4*>(o) = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
-    }
+    const int rows = min(16, R - pd.row0);
+    // lanes per row: 64 / (rows rounded up to a power of two), at most D / 4
+    if (rows > 8)
+        merge_pieces<D, 16, D / 16, (D == 128 ? 2 : 4)>(a, pd, lane, rows, W, P);
+    else if (rows > 4)
+        merge_pieces<D, 16, D / 32, (D == 128 ? 4 : 8)>(a, pd, lane, rows, W, P);
+    else if (rows > 2 || D == 64)
+        merge_pieces<D, 16, (D == 128 ? 2 : 1), (D == 128 ? 8 : 16)>(a, pd, lane, rows, W, P);
+    else
+        merge_pieces<D, 16, 1, 16>(a, pd, lane, rows, W, P);
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1438,7 +1491,7 @@ decode_mfa(const Args a, const int R, const int n_rb)
         Pending pd;
         if (mfa_piece<D>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
-            merge_rows<D, 16>(a, pd, lane, R, W, P);
+            arrive_and_merge16<D>(a, pd, lane, R, W, P);
         }
     }
 }
