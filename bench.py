@@ -128,6 +128,7 @@ def main(argv=None):
     ap.add_argument("--workload", default=gi.HEADLINE, choices=sorted(gi.WORKLOADS))
     ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_qk"])
+    ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "combine"])
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -163,7 +164,8 @@ def main(argv=None):
     path = {"auto": gqa.PATH_AUTO, "valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA,
             "mfma_qk": gqa.PATH_MFMA_QK}[args.path]
     shape = gqa.shape_of(x["q"], x["k"])
-    plan = gqa.plan(shape, path=path, workgroups=args.workgroups)
+    merge = {"auto": gqa.MERGE_AUTO, "kernel": gqa.MERGE_IN_KERNEL, "combine": gqa.MERGE_COMBINE}[args.merge]
+    plan = gqa.plan(shape, path=path, workgroups=args.workgroups, merge=merge)
     log("[bench] plan %s" % plan)
     out = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -171,7 +173,7 @@ def main(argv=None):
 
     def call():
         gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
-                   workgroups=args.workgroups, stream=stream)
+                   workgroups=args.workgroups, merge=merge, stream=stream)
 
     for _ in range(args.warmup):
         if not args.no_flush:
@@ -268,6 +270,7 @@ def main(argv=None):
             "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
+            "combine_kernel": bool(plan["combine"]),
         },
         "us_per_step": round(ms * 1e3, 2),
         "timing": "device time per step: K steps back to back after cache sweeps, minus the sweeps alone",

@@ -21,6 +21,7 @@ import threading
 
 __all__ = ["decode", "plan", "workspace_bytes", "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
+           "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
            "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libgqa.so")
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
 GQA_F32, GQA_BF16 = 0, 1
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
+MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",
@@ -50,13 +52,14 @@ class Shape(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
                 ("rows_per_group", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
-                ("row_block", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+                ("row_block", ctypes.c_int32), ("combine", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -122,18 +125,19 @@ def make_shape(B, H, G, sq, T, D, q_dtype=GQA_BF16, kv_dtype=GQA_BF16, out_dtype
     return Shape(B, H, G, sq, T, D, q_dtype, kv_dtype, out_dtype)
 
 
-def _options(path=PATH_AUTO, workgroups=0):
+def _options(path=PATH_AUTO, workgroups=0, merge=0):
     o = Options()
     o.path = int(path)
     o.workgroups = int(workgroups)
+    o.merge = int(merge)
     return o
 
 
-def plan(shape: Shape, path=PATH_AUTO, workgroups=0) -> dict:
+def plan(shape: Shape, path=PATH_AUTO, workgroups=0, merge=0) -> dict:
     """The planner's launch decisions for ``shape`` (host only)."""
     lib = load_library()
     info = PlanInfo()
-    opts = _options(path, workgroups)
+    opts = _options(path, workgroups, merge)
     _check(lib.gqa_plan(ctypes.byref(shape), ctypes.byref(opts), ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
 
@@ -155,7 +159,7 @@ def shape_of(q, k_cache, out_dtype=None) -> Shape:
 
 
 def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
-           path=PATH_AUTO, workgroups=0, workspace=None, stream=None):
+           path=PATH_AUTO, workgroups=0, merge=0, workspace=None, stream=None):
     """Grouped-query attention for one decode step (see module docstring).
 
     Runs asynchronously on ``stream`` (default: torch's current stream).
@@ -163,6 +167,7 @@ def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
     ``workspace_bytes(shape_of(q, k_cache))`` bytes, zero-filled before its
     first use (each call leaves it zeroed); default: library-owned.
     ``workgroups``: kernel grid size (0 = the planner's choice).
+    ``merge``: MERGE_AUTO, MERGE_IN_KERNEL or MERGE_COMBINE (matrix-core path).
     """
     import torch
     lib = load_library()
@@ -196,7 +201,7 @@ def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    opts = _options(path, workgroups)
+    opts = _options(path, workgroups, merge)
     ws_ptr, ws_len = None, 0
     if workspace is not None:
         if not workspace.is_cuda or workspace.device != dev:

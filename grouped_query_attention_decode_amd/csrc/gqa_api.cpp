@@ -78,12 +78,15 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         return fail(GQA_ERR_INVALID_ARG, "B * H * sq * D too large");
     const int64_t R64 = (int64_t)(s->H / s->G) * s->sq;
     if (R64 > (1 << 20)) return fail(GQA_ERR_INVALID_ARG, "(H/G)*sq too large");
-    int path_req = GQA_PATH_AUTO, wg_req = 0;
+    int path_req = GQA_PATH_AUTO, wg_req = 0, merge_req = GQA_MERGE_AUTO;
     if (o) {
         path_req = o->path;
         wg_req = o->workgroups;
-        for (int i = 0; i < 6; ++i)
+        merge_req = o->merge;
+        for (int i = 0; i < 5; ++i)
             if (o->reserved[i] != 0) return fail(GQA_ERR_INVALID_ARG, "options.reserved must be zero");
+        if (merge_req < GQA_MERGE_AUTO || merge_req > GQA_MERGE_COMBINE)
+            return fail(GQA_ERR_INVALID_ARG, "unknown merge mode %d", merge_req);
         if (path_req < GQA_PATH_AUTO || path_req > GQA_PATH_MFMA_QK)
             return fail(GQA_ERR_INVALID_ARG, "unknown path %d", path_req);
         if (wg_req < 0) return fail(GQA_ERR_INVALID_ARG, "workgroups must be >= 0");
@@ -106,7 +109,9 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     p->R = R;
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
     if (p->path == gqa::Path::MFMA_QK && p->row_block < 4) p->row_block = 4;   // one k group of the 16x16 tile
-    if (p->path == gqa::Path::MFMA) p->row_block = 16;   // the query rows of one 16x16 tile
+    // matrix-core path: 16, 32 or 64 query rows (one to four 16-row MFMA
+    // blocks) share each K/V tile a wave reads
+    if (p->path == gqa::Path::MFMA) p->row_block = R <= 16 ? 16 : R <= 32 ? 32 : 64;
     p->n_rb = (R + p->row_block - 1) / p->row_block;
     if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
         return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
@@ -133,7 +138,22 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     if (P > (1 << 20)) P = 1 << 20;
     if (P < 1) P = 1;
     p->grid = s->B > 0 ? P : 0;
-    p->part_bytes = round_up((size_t)P * 2 * (p->row_block * s->D + 16) * sizeof(float), 256);
+    // Merges by the last arriving wave read every piece's partial alone; when
+    // a segment's partials are large (many pieces of many live rows) a
+    // second kernel merges them, one wave per query row, instead.
+    {
+        const int64_t segs = (int64_t)s->B * s->G * p->n_rb;
+        const int64_t pieces = segs > 0 ? P / segs + 2 : 1;
+        const int64_t live = R < p->row_block ? R : p->row_block;
+        p->deferred = (p->path == gqa::Path::MFMA && pieces * live * s->D * 4 > gqa::kMergeBytesInKernel) ? 1 : 0;
+    }
+    if (merge_req == GQA_MERGE_IN_KERNEL) p->deferred = 0;
+    if (merge_req == GQA_MERGE_COMBINE) {
+        if (p->path != gqa::Path::MFMA)
+            return fail(GQA_ERR_UNSUPPORTED, "the combine kernel serves the MFMA path only");
+        p->deferred = 1;
+    }
+    p->part_bytes = round_up((size_t)P * 2 * gqa::slot_floats(p->row_block, s->D) * sizeof(float), 256);
     p->ws_bytes = gqa::kCounterRegion + p->part_bytes;
     return GQA_OK;
 }
@@ -221,6 +241,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.sq = shape->sq;
     a.T = shape->T;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.deferred = plan.deferred;
 
     hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -275,6 +296,7 @@ gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_p
     plan->rows_per_group = p.R;
     plan->row_blocks = p.n_rb;
     plan->row_block = p.row_block;
+    plan->combine = p.deferred;
     plan->workspace_bytes = p.ws_bytes;
     return ok();
 }

@@ -14,12 +14,17 @@ constexpr int kMaxRowBlock = 16;   // query rows per VALU segment
 constexpr int kMaxSegments = 1 << 18;  // (sequence, KV head, row block) triples per call
 constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (measured best)
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
+constexpr int64_t kMergeBytesInKernel = 64 << 10;  // larger merges go to the combine kernel
 // The workspace starts with one arrival counter per possible segment, at a
 // fixed place whatever the shape, so counters never land on another call's
 // partials; the partials follow.
 constexpr size_t kCounterRegion = (size_t)kMaxSegments * sizeof(int32_t);
 
 enum class Path : int { VALU = 1, MFMA = 2, MFMA_QK = 3 };
+
+// Floats in one partial slot: rb rows of d values, then the rows'
+// log2-sum-exp padded to a multiple of 16 (slots stay 64-byte aligned).
+__host__ __device__ constexpr int slot_floats(int rb, int d) { return rb * d + (rb > 16 ? rb : 16); }
 
 struct Plan {
     Path path;
@@ -29,7 +34,8 @@ struct Plan {
     int row_block;      // rows per segment (power of two <= 16; 16 on the MFMA path)
     int n_rb;           // row blocks per (b, g)
     int64_t grid;       // workgroups (one wave each) P
-    size_t part_bytes;  // partials: P * 2 * (row_block * D + 16) floats
+    int deferred;       // 1: split segments are merged by a second, parallel kernel
+    size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };
 
@@ -43,6 +49,7 @@ struct Args {
     int32_t* counters;  // [kMaxSegments], zero before and after every call
     int B, H, G, sq, T;
     float scale_log2;   // scale * log2(e): scores kept in base-2 exponent units
+    int deferred;       // leave every split segment's partials for the combine kernel
 };
 
 // Queue the decode kernel on stream.

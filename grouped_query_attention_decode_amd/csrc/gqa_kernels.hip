@@ -390,11 +390,11 @@ struct Pending {
 // Partial slot of workgroup q for the segment starting at unit off: slot 0
 // when the segment holds q's first unit, else slot 1 (the segment that runs
 // past q's last unit).  A slot is RB rows of D values (16-byte aligned) and
-// then RB log2-sum-exp values padded to 16 floats; offset in floats.
+// then RB log2-sum-exp values (at least 16 floats); offset in floats.
 template <int D, int RB>
 __device__ __forceinline__ int slot_base(int q, long long off, long long W, int P)
 {
-    return (q * 2 + (wg_start(W, P, q) >= off ? 0 : 1)) * (RB * D + 16);
+    return (q * 2 + (wg_start(W, P, q) >= off ? 0 : 1)) * slot_floats(RB, D);
 }
 
 // The same for the pieces of one segment, q = p_first + k: only the first
@@ -403,7 +403,7 @@ __device__ __forceinline__ int slot_base(int q, long long off, long long W, int 
 template <int D, int RB>
 __device__ __forceinline__ int piece_slot(int p_first, int k, bool tail1)
 {
-    return ((p_first + k) * 2 + (k == 0 && tail1 ? 1 : 0)) * (RB * D + 16);
+    return ((p_first + k) * 2 + (k == 0 && tail1 ? 1 : 0)) * slot_floats(RB, D);
 }
 
 // One step of the running log-sum-exp merge, branch-free (so that the
@@ -1183,7 +1183,10 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // tiles skip the rescale.
 constexpr float kSlack = 8.0f;
 
-constexpr int kMfaBuffers = 3;   // tiles held in registers per wave (measured best)
+// K/V tiles held in registers per wave: 3 (two in flight) measured best; with
+// four 16-row query blocks the accumulators need the room, so 2.
+template <int NB>
+constexpr int mfa_buffers() { return NB >= 4 ? 2 : 3; }
 
 template <int D>
 struct MfaShared {
@@ -1227,11 +1230,12 @@ __device__ __forceinline__ float sum_x32(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One piece of segment (b, g, rb) -- cache rows [ta, tb) for query rows
-// 16 rb .. 16 rb + 15 -- streamed in 16-row tiles with the next two tiles'
-// loads in flight; then written out, or left as a partial (returned in *pd,
-// stores issued, nothing waited for).
-template <int D>
+// One piece of segment (b, g, rb) -- cache rows [ta, tb) for the RB = 16 NB
+// query rows RB rb .. RB rb + RB - 1 -- streamed in 16-row tiles with the
+// next tiles' loads in flight; then written out, or left as a partial
+// (returned in *pd, stores issued, nothing waited for).  The NB 16-row
+// blocks share every K/V tile: it is read once for all of them.
+template <int D, int NB>
 __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
                                           long long W, int P, int p, Pending* pd)
 {
@@ -1240,31 +1244,39 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     constexpr int SE = MfaShared<D>::SE;
     constexpr int CPR = D / 8;           // 16-byte chunks per cache row
     constexpr int NLV = 16 * CPR / kWave;   // V loads per lane per tile
-    constexpr int RB = 16;
+    constexpr int RB = 16 * NB;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int col = lane & 15;           // query row of this lane (score / output column)
+    const int col = lane & 15;           // query row of this lane within a block
     const int kg = lane >> 4;            // k group: cache rows 4 kg .. 4 kg + 3 of a tile
     const int ta = pc.ta, tb = pc.tb;
     const int row0 = pc.rb * RB;
     const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
-    const bool live = row0 + col < R;
 
-    // B operand of the score product: query row `col`, zero past R
-    uint4 qb[NK];
-    {
-        const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live ? col : 0)) * D + 8 * kg) * 2;
+    // B operands of the score product: query row 16 nb + col, zero past R
+    uint4 qb[NB][NK];
+    bool live[NB];
+    int last[NB];
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = row0 + 16 * nb + col;
+        live[nb] = r < R;
+        last[nb] = live[nb] ? pc.L - a.sq + (r % a.sq) : -1;
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.0f;
+        const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live[nb] ? 16 * nb + col : 0)) * D + 8 * kg) * 2;
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
             const uint4 v = load16(qp + 64 * s);
-            qb[s] = live ? v : make_uint4(0, 0, 0, 0);
+            qb[nb][s] = live[nb] ? v : make_uint4(0, 0, 0, 0);
         }
     }
-    const int last = live ? pc.L - a.sq + ((row0 + col) % a.sq) : -1;
-    float m_run = -INFINITY, l_run = 0.0f;
-    f32x4_t acc[NC];
+    f32x4_t acc[NB][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[nb][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
     const char* kbase = static_cast<const char*>(a.k) + (slab + 8 * kg) * 2;
@@ -1292,49 +1304,56 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             const int c = lane + kWave * j;
             *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
         }
-        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        s16x4_t ph[NB], pl[NB];
 #pragma unroll
-        for (int s = 0; s < NK; ++s)
-            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
-                                                         __builtin_bit_cast(bf16x8_t, qb[s]), s4, 0, 0, 0);
-        float sc[4];
-        float mx = -INFINITY;
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int t = t0 + 4 * kg + jj;
-            sc[jj] = (t < tb && t <= last) ? s4[jj] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sc[jj]);
+            for (int s = 0; s < NK; ++s)
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                             __builtin_bit_cast(bf16x8_t, qb[nb][s]), s4, 0, 0, 0);
+            float sc[4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int t = t0 + 4 * kg + jj;
+                sc[jj] = (t < tb && t <= last[nb]) ? s4[jj] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sc[jj]);
+            }
+            mx = max_x32(max_x16(mx));
+            // the four lanes of a query row take the same decision
+            const bool need = mx > m_run[nb] + kSlack;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float al = need ? __builtin_amdgcn_exp2f(m_run[nb] - mx) : 1.0f;
+                m_run[nb] = need ? mx : m_run[nb];
+                l_run[nb] *= al;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) acc[nb][c] *= al;
+            }
+            float pv[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                pv[jj] = (sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run[nb]);
+                l_run[nb] += pv[jj];
+            }
+            // p = hi + lo, both bf16
+            const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
+            const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
+            const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
+            const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
+            ph[nb] = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
+            pl[nb] = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
         }
-        mx = max_x32(max_x16(mx));
-        // the four lanes of a query row take the same decision
-        const bool need = mx > m_run + kSlack;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-            const float al = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
-            m_run = need ? mx : m_run;
-            l_run *= al;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) acc[c] *= al;
-        }
-        float pv[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            pv[jj] = (sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run);
-            l_run += pv[jj];
-        }
-        // p = hi + lo, both bf16
-        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
-        const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
-        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
-        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
-        const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
-        const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
         const uint16_t* vr = sm.vt + 4 * kg * SE + col;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const s16x4_t va = {(short)vr[16 * c], (short)vr[SE + 16 * c], (short)vr[2 * SE + 16 * c],
                                 (short)vr[3 * SE + 16 * c]};
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[c], 0, 0, 0);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[c], 0, 0, 0);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[nb], acc[nb][c], 0, 0, 0);
+                acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[nb], acc[nb][c], 0, 0, 0);
+            }
         }
     };
 
@@ -1342,17 +1361,18 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     // while one is computed.  The loads are unconditional (rows clamped into
     // the piece), so the compiler waits for exactly the oldest tile.
     {
-        uint4 kb[kMfaBuffers][NK], vb[kMfaBuffers][NLV];
+        constexpr int NBUF = mfa_buffers<NB>();
+        uint4 kb[NBUF][NK], vb[NBUF][NLV];
         int t0 = ta;
         const int ntile = (tb - ta + 15) / 16;
 #pragma unroll
-        for (int u = 0; u < kMfaBuffers - 1; ++u) load_tile(t0 + 16 * u, kb[u], vb[u]);
-        for (int it = 0; it < ntile; it += kMfaBuffers) {
+        for (int u = 0; u < NBUF - 1; ++u) load_tile(t0 + 16 * u, kb[u], vb[u]);
+        for (int it = 0; it < ntile; it += NBUF) {
 #pragma unroll
-            for (int u = 0; u < kMfaBuffers; ++u) {
+            for (int u = 0; u < NBUF; ++u) {
                 if (it + u >= ntile) break;
-                const int nxt = (u + kMfaBuffers - 1) % kMfaBuffers;
-                load_tile(t0 + 16 * (kMfaBuffers - 1), kb[nxt], vb[nxt]);
+                const int nxt = (u + NBUF - 1) % NBUF;
+                load_tile(t0 + 16 * (NBUF - 1), kb[nxt], vb[nxt]);
                 compute_tile(t0, kb[u], vb[u]);
                 t0 += 16;
             }
@@ -1360,28 +1380,38 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     }
 
     // ---- end of the piece ------------------------------------------------------
-    const float l = sum_x32(sum_x16(l_run));
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float inv[NB], lse[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l = sum_x32(sum_x16(l_run[nb]));
+        inv[nb] = l > 0.0f ? 1.0f / l : 0.0f;
+        lse[nb] = l > 0.0f ? m_run[nb] + __log2f(l) : -INFINITY;
+    }
     const int p_first = wg_of(pc.off, W, P);
     const int npieces = wg_of(pc.off + pc.L - 1, W, P) - p_first + 1;
     if (npieces == 1) {
-        if (live) {
-            float* o = a.out + (qrow0 + col) * D + 4 * kg;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[c] * inv;
+        for (int nb = 0; nb < NB; ++nb) {
+            if (!live[nb]) continue;
+            float* o = a.out + (qrow0 + 16 * nb + col) * D + 4 * kg;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[nb][c] * inv[nb];
         }
         return false;
     }
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
     const int mine = slot_base<D, RB>(p, pc.off, W, P);
-    if (live) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        if (!live[nb]) continue;
+        const int r = 16 * nb + col;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const f32x4_t o = acc[c] * inv;
+            const f32x4_t o = acc[nb][c] * inv[nb];
             const float ov[4] = {o[0], o[1], o[2], o[3]};
-            store4_coherent(part, mine + col * D + 16 * c + 4 * kg, ov);
+            store4_coherent(part, mine + r * D + 16 * c + 4 * kg, ov);
         }
-        if (kg == 0) store_coherent(part, mine + RB * D + col, l > 0.0f ? m_run + __log2f(l) : -INFINITY);
+        if (kg == 0) store_coherent(part, mine + RB * D + r, lse[nb]);
     }
     pd->seg = (pc.b * a.G + pc.g) * n_rb + pc.rb;
     pd->p_first = p_first;
@@ -1397,13 +1427,13 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 // spread over the wave, LPR lanes per row, NF float4 of the row per lane;
 // KB pieces are loaded at a time, all their loads in flight together.
 template <int D, int RB, int NF, int KB>
-__device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, int lane, int rows, long long W,
-                                             int P)
+__device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, int lane, int r0, int rows,
+                                             long long W, int P)
 {
     constexpr int LPR = D / (4 * NF);
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
     const int i = lane / LPR;
-    const int ic = min(i, rows - 1);
+    const int ic = r0 + min(i, rows - 1);
     const int e0 = (lane % LPR) * 4 * NF;
     float M = -INFINITY, den = 0.0f;
     float num[NF][4];
@@ -1434,7 +1464,7 @@ __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, i
     }
     if (i < rows) {
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        float* o = a.out + (pd.qrow0 + i) * D + e0;
+        float* o = a.out + (pd.qrow0 + r0 + i) * D + e0;
 #pragma unroll
         for (int f = 0; f < NF; ++f)
             *reinterpret_cast<float4*>(o + 4 * f) =
@@ -1442,32 +1472,37 @@ __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, i
     }
 }
 
-// Count this wave's arrival for a pending segment of RB = 16 rows; the last
-// arrival merges (choosing the lane layout by the number of live rows) and
-// resets the counter.  The caller has waited for its own partial stores.
-template <int D>
-__device__ __forceinline__ void arrive_and_merge16(const Args& a, const Pending& pd, int lane, int R, long long W,
-                                                   int P)
+// Count this wave's arrival for a pending segment of RB rows; the last
+// arrival merges, 16 rows at a time (choosing the lane layout by the number
+// of live rows), and resets the counter.  The caller has waited for its own
+// partial stores.
+template <int D, int RB>
+__device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pending& pd, int lane, int R, long long W,
+                                                     int P)
 {
     int old = 0;
     if (lane == 0)
         old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
     if (old != pd.npieces - 1) return;
-    const int rows = min(16, R - pd.row0);
-    // lanes per row: 64 / (rows rounded up to a power of two), at most D / 4
-    if (rows > 8)
-        merge_pieces<D, 16, D / 16, (D == 128 ? 2 : 4)>(a, pd, lane, rows, W, P);
-    else if (rows > 4)
-        merge_pieces<D, 16, D / 32, (D == 128 ? 4 : 8)>(a, pd, lane, rows, W, P);
-    else if (rows > 2 || D == 64)
-        merge_pieces<D, 16, (D == 128 ? 2 : 1), (D == 128 ? 8 : 16)>(a, pd, lane, rows, W, P);
-    else
-        merge_pieces<D, 16, 1, 16>(a, pd, lane, rows, W, P);
+    const int live_rows = min(RB, R - pd.row0);
+    for (int r0 = 0; r0 < live_rows; r0 += 16) {
+        const int rows = min(16, live_rows - r0);
+        // lanes per row: 64 / (rows rounded up to a power of two), at most D / 4;
+        // about 32 to 48 loads of a batch in flight per lane
+        if (rows > 8)
+            merge_pieces<D, RB, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, W, P);
+        else if (rows > 4)
+            merge_pieces<D, RB, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, W, P);
+        else if (rows > 2 || D == 64)
+            merge_pieces<D, RB, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, W, P);
+        else
+            merge_pieces<D, RB, 1, 16>(a, pd, lane, r0, rows, W, P);
+    }
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
+template <int D, int NB>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const Args a, const int R, const int n_rb)
 {
@@ -1489,10 +1524,73 @@ decode_mfa(const Args a, const int R, const int n_rb)
     Piece pc;
     while (it.next(a, sm.lens, lbase, pc)) {
         Pending pd;
-        if (mfa_piece<D>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
+        if (mfa_piece<D, NB>(a, sm, R, n_rb, pc, W, P, p, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
-            arrive_and_merge16<D>(a, pd, lane, R, W, P);
+            arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, W, P);
         }
+    }
+}
+
+// Combine pass for a deferred plan: one wave per (segment, query row) of a
+// split segment merges the row's partials, in piece order (the same
+// log2-sum-exp merge as the in-kernel one).  Lane l holds elements
+// 4 l .. 4 l + 3 of the row; KB pieces' loads are in flight together.
+template <int D, int RB>
+__global__ void __launch_bounds__(kWave)
+combine_rows(const Args a, const int R, const int n_rb, const int P)
+{
+    constexpr int KB = 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = blockIdx.x % RB;
+    const long long seg = blockIdx.x / RB;
+    const int rb = (int)(seg % n_rb);
+    const int g = (int)((seg / n_rb) % a.G);
+    const int b = (int)(seg / ((long long)n_rb * a.G));
+    const int row = rb * RB + r;
+    if (row >= R) return;
+    const int L = clamp_len(a.seq_lens, b, a.T);
+    if (L == 0) return;
+    // units before sequence b, and in total (every wave of the grid agrees)
+    long long before = 0, tot = 0;
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
+        const int bb = b0 + lane;
+        const uint32_t Lb = bb < a.B ? (uint32_t)clamp_len(a.seq_lens, bb, a.T) : 0u;
+        tot += wave_sum_u32(Lb);
+        before += wave_sum_u32(bb < b ? Lb : 0u);
+    }
+    const long long units = (long long)a.G * n_rb;
+    const long long W = tot * units;
+    const long long off = before * units + ((long long)g * n_rb + rb) * L;
+    const int p_first = wg_of(off, W, P);
+    const int npieces = wg_of(off + L - 1, W, P) - p_first + 1;
+    if (npieces == 1) return;                 // written by its piece
+    const bool tail1 = wg_start(W, P, p_first) < off;
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const int e = 4 * min(lane, D / 4 - 1);
+    float M = -INFINITY, den = 0.0f;
+    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < npieces; k0 += KB) {
+        float lse[KB], ov[KB][4];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int base = piece_slot<D, RB>(p_first, min(k0 + kk, npieces - 1), tail1);
+            lse[kk] = load_coherent(part, base + RB * D + r);
+            load4_coherent(part, base + r * D + e, ov[kk]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            float w;
+            const float sc = lse_step(M, k0 + kk < npieces ? lse[kk] : -INFINITY, &w);
+            den = fmaf(den, sc, w);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) num[q] = fmaf(num[q], sc, w * ov[kk][q]);
+        }
+    }
+    if (lane < D / 4) {
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        const int64_t qrow = (int64_t)b * a.H * a.sq + (int64_t)g * R + row;
+        *reinterpret_cast<float4*>(a.out + qrow * D + e) =
+            make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
     }
 }
 
@@ -1528,8 +1626,13 @@ static DecodeFn pick_mqk(int rb)
 static DecodeFn pick(const Plan& p)
 {
     if (p.path == Path::MFMA) {
-        if (!p.kv_bf16 || p.row_block != 16) return nullptr;
-        return p.D == 64 ? decode_mfa<64> : decode_mfa<128>;
+        if (!p.kv_bf16) return nullptr;
+        switch (p.row_block) {
+        case 16: return p.D == 64 ? decode_mfa<64, 1> : decode_mfa<128, 1>;
+        case 32: return p.D == 64 ? decode_mfa<64, 2> : decode_mfa<128, 2>;
+        case 64: return p.D == 64 ? decode_mfa<64, 4> : decode_mfa<128, 4>;
+        default: return nullptr;
+        }
     }
     if (p.path == Path::MFMA_QK) {
         if (!p.kv_bf16) return nullptr;
@@ -1561,12 +1664,34 @@ int cache_rows_per_wave_tile(const Plan& p)
     return kSlotsPerLane * (kWave / lpt);
 }
 
+typedef void (*CombineFn)(const Args, int, int, int);
+
+static CombineFn pick_combine(const Plan& p)
+{
+    if (p.path != Path::MFMA) return nullptr;
+    switch (p.row_block) {
+    case 16: return p.D == 64 ? combine_rows<64, 16> : combine_rows<128, 16>;
+    case 32: return p.D == 64 ? combine_rows<64, 32> : combine_rows<128, 32>;
+    case 64: return p.D == 64 ? combine_rows<64, 64> : combine_rows<128, 64>;
+    default: return nullptr;
+    }
+}
+
 hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
 {
     if (p.grid <= 0) return hipSuccess;
     DecodeFn fn = pick(p);
     if (!fn) return hipErrorInvalidValue;
+    CombineFn comb = nullptr;
+    if (p.deferred) {
+        comb = pick_combine(p);
+        if (!comb || a.deferred != 1) return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave), 0, stream, a, p.R, p.n_rb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !comb) return e;
+    const int64_t rows = (int64_t)a.B * a.G * p.n_rb * p.row_block;
+    hipLaunchKernelGGL(comb, dim3((unsigned)rows), dim3(kWave), 0, stream, a, p.R, p.n_rb, (int)p.grid);
     return hipGetLastError();
 }
 

@@ -80,13 +80,22 @@ typedef enum {
                              V sum; bf16 inputs only                                  */
 } gqa_path_t;
 
+/* Merge of the pieces of a (sequence, KV head) segment split over several
+ * workgroups (GQA_PATH_MFMA only; the other paths always merge in-kernel). */
+typedef enum {
+    GQA_MERGE_AUTO = 0,      /* in-kernel while a segment's partials are small       */
+    GQA_MERGE_IN_KERNEL = 1, /* the last arriving wave merges all pieces              */
+    GQA_MERGE_COMBINE = 2    /* a second kernel merges, one wave per query row        */
+} gqa_merge_t;
+
 /* Optional knobs; zero-initialise for defaults. */
 typedef struct {
     int32_t path;        /* gqa_path_t                                                 */
     int32_t workgroups;  /* workgroups of the (single, persistent) kernel; 0 = as many
                             as the GPU holds at once.  Each takes an equal share of the
                             cache rows, so any value gives the same result to rounding. */
-    int32_t reserved[6]; /* must be zero                                               */
+    int32_t merge;       /* gqa_merge_t: who merges a segment split over workgroups  */
+    int32_t reserved[5]; /* must be zero                                               */
 } gqa_options_t;
 
 /* What the planner decided for a shape (filled by gqa_plan). */
@@ -96,7 +105,9 @@ typedef struct {
     int32_t rows_per_group; /* (H/G)*sq: query rows sharing one KV head                */
     int32_t row_blocks;     /* segments per (b, KV head) along those rows              */
     int32_t row_block;      /* query rows per segment                                  */
-    int32_t reserved[3];
+    int32_t combine;        /* 1: split segments are merged by a second kernel (one
+                               wave per query row); 0: by the last arriving wave      */
+    int32_t reserved[2];
     uint64_t workspace_bytes; /* device scratch the call needs                        */
 } gqa_plan_t;
 

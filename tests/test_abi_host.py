@@ -92,6 +92,44 @@ def test_plan_row_blocks_for_large_groups(lib):
     assert p["rows_per_group"] == 3 and p["row_block"] == 4
 
 
+def test_plan_matrix_path_row_blocks(lib):
+    """The matrix-core path packs 16, 32 or 64 query rows per segment, so the
+    K/V of a group is read once for up to 64 rows."""
+    cases = [  # (H, G, sq) -> rows, row block, row blocks
+        ((32, 8, 1), 4, 16, 1),
+        ((32, 4, 2), 16, 16, 1),
+        ((32, 1, 1), 32, 32, 1),
+        ((6, 1, 3), 18, 32, 1),
+        ((32, 1, 2), 64, 64, 1),
+        ((32, 1, 3), 96, 64, 2),
+    ]
+    for (H, G, sq), rows, rb, nrb in cases:
+        p = gqa.plan(_shape(H=H, G=G, sq=sq))
+        assert p["path"] == gqa.PATH_MFMA
+        assert (p["rows_per_group"], p["row_block"], p["row_blocks"]) == (rows, rb, nrb), (H, G, sq)
+        # slots: rb rows of 128 values, then max(rb, 16) log-sum-exp floats
+        assert p["workspace_bytes"] == (1 << 20) + _round256(p["workgroups"] * 2 * (rb * 128 + max(rb, 16)) * 4)
+
+
+def test_plan_merge_mode(lib):
+    """Small merges stay in the decode kernel; a segment split into many
+    pieces of many live rows goes to the combine kernel; both can be forced."""
+    assert gqa.plan(_shape(B=32))["combine"] == 0                      # 4 live rows
+    mqa = _shape(B=64, H=32, G=1, T=8192)                                # 32 live rows
+    assert gqa.plan(mqa)["combine"] == 1
+    assert gqa.plan(mqa, merge=gqa.MERGE_IN_KERNEL)["combine"] == 0
+    assert gqa.plan(_shape(B=32), merge=gqa.MERGE_COMBINE)["combine"] == 1
+    f32 = _shape(q_dtype=gqa.GQA_F32, kv_dtype=gqa.GQA_F32)
+    with pytest.raises(gqa.GqaError) as ei:
+        gqa.plan(f32, merge=gqa.MERGE_COMBINE)
+    assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+    with pytest.raises(gqa.GqaError) as ei:
+        gqa.plan(_shape(), merge=3)
+    assert ei.value.status == gqa.GQA_ERR_INVALID_ARG
+    # the combine flag does not change the workspace
+    assert gqa.plan(mqa)["workspace_bytes"] == gqa.plan(mqa, merge=gqa.MERGE_IN_KERNEL)["workspace_bytes"]
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(H=30, G=8), gqa.GQA_ERR_INVALID_ARG),
     (dict(G=0), gqa.GQA_ERR_INVALID_ARG),

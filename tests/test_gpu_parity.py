@@ -111,6 +111,9 @@ EDGE = [
     (4, 8, 2, 128, 64, 1, "bf16", [0, 1, 64, 200]),      # empty, single row, full, clamped
     (2, 8, 4, 64, 50, 3, "bf16", [2, 3]),                # rows that see nothing
     (1, 4, 2, 128, 1, 1, "f32", None),                   # T = 1
+    (2, 32, 1, 128, 300, 2, "bf16", [300, 123]),         # R=64: four 16-row blocks per wave
+    (2, 32, 1, 64, 200, 3, "bf16", [200, 50]),           # R=96: two 64-row segments, second half live
+    (2, 24, 1, 128, 150, 2, "bf16", [150, 149]),         # R=48: last 16-row block padding only
 ]
 
 
@@ -196,6 +199,23 @@ def test_split_invariance_and_determinism(gqa, orc, dt, path_name):
     for _ in range(3):
         again = _run(gqa, xc, workgroups=97, path=path)
         assert torch.equal(again, outs[3])
+
+
+@pytest.mark.parametrize("H,G,sq,D", [(32, 8, 1, 128), (32, 1, 1, 128), (32, 1, 2, 64), (24, 1, 2, 128)])
+def test_merge_modes_match_oracle(gqa, orc, H, G, sq, D):
+    """The in-kernel merge and the combine kernel both give the oracle's
+    result at several splits, and each is deterministic."""
+    x = gi.make_custom(4, H, G, D, 777, sq, dtype="bf16", seed=300 + H + G + sq,
+                       seq_lens=[777, 3, 400, 129])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
+    xc = _to(x, "cuda")
+    for P in (5, 64, 300):
+        outs = {}
+        for m in (gqa.MERGE_IN_KERNEL, gqa.MERGE_COMBINE):
+            o = _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=m)
+            _compare(o, want, TOL["bf16"], "P=%d merge=%d" % (P, m))
+            assert torch.equal(o, _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=m))
+            outs[m] = o
 
 
 def test_explicit_workspace_matches_library_workspace(gqa):
