@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -125,15 +126,23 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // One-wave workgroups: kWavesPerCU per compute unit (fewer if they do not
     // fit) -- enough loads in flight to saturate HBM; more waves only add
     // pieces, and so partials and merges.
+    // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
+    // then one wave on each of the four SIMDs of a compute unit.
+    const int want = (p->path == gqa::Path::MFMA && p->row_block >= 64) ? 4 : gqa::kWavesPerCU;
     int occ = gqa::resident_groups_per_cu(*p);
-    if (occ <= 0 || occ > gqa::kWavesPerCU) occ = gqa::kWavesPerCU;
+    if (occ <= 0 || occ > want) occ = want;
     int64_t P = (int64_t)device_compute_units() * occ;
     const int64_t by_size = (max_units + min_share - 1) / min_share;
     if (P > by_size) P = by_size;
-    // A split segment is merged by one wave reading every piece's partial:
-    // keep the pieces per segment (at full length) bounded.
+    // A split segment merged in-kernel is merged by one wave reading every
+    // piece's partial: keep the pieces per segment (at full length) bounded
+    // unless the combine kernel (one wave per query row) does the merging.
     const int64_t by_merge = (int64_t)s->B * s->G * p->n_rb * gqa::kMaxPiecesPerSegment;
-    if (P > by_merge) P = by_merge;
+    const int64_t live = R < p->row_block ? R : p->row_block;
+    const bool big_merges = p->path == gqa::Path::MFMA &&
+                            (std::min(P, by_merge) / std::max<int64_t>(1, (int64_t)s->B * s->G * p->n_rb) + 2) *
+                                    live * s->D * 4 > gqa::kMergeBytesInKernel;
+    if (P > by_merge && !(big_merges && merge_req != GQA_MERGE_IN_KERNEL)) P = by_merge;
     if (wg_req > 0) P = wg_req;
     if (P > (1 << 20)) P = 1 << 20;
     if (P < 1) P = 1;
@@ -144,7 +153,6 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     {
         const int64_t segs = (int64_t)s->B * s->G * p->n_rb;
         const int64_t pieces = segs > 0 ? P / segs + 2 : 1;
-        const int64_t live = R < p->row_block ? R : p->row_block;
         p->deferred = (p->path == gqa::Path::MFMA && pieces * live * s->D * 4 > gqa::kMergeBytesInKernel) ? 1 : 0;
     }
     if (merge_req == GQA_MERGE_IN_KERNEL) p->deferred = 0;
