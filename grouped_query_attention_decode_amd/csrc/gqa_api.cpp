@@ -144,7 +144,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
                                     live * s->D * 4 > gqa::kMergeBytesInKernel;
     if (P > by_merge && !(big_merges && merge_req != GQA_MERGE_IN_KERNEL)) P = by_merge;
     if (wg_req > 0) P = wg_req;
-    if (P > (1 << 20)) P = 1 << 20;
+    if (P > (1 << 16)) P = 1 << 16;
     if (P < 1) P = 1;
     p->grid = s->B > 0 ? P : 0;
     // Merges by the last arriving wave read every piece's partial alone; when
@@ -161,7 +161,9 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
             return fail(GQA_ERR_UNSUPPORTED, "the combine kernel serves the MFMA path only");
         p->deferred = 1;
     }
-    p->part_bytes = round_up((size_t)P * 2 * gqa::slot_floats(p->row_block, s->D) * sizeof(float), 256);
+    // matrix-core path: a slot holds only the live rows, min(row_block, R)
+    p->slot_rows = (p->path == gqa::Path::MFMA && R < p->row_block) ? R : p->row_block;
+    p->part_bytes = round_up((size_t)P * 2 * gqa::slot_floats(p->slot_rows, s->D) * sizeof(float), 256);
     p->ws_bytes = gqa::kCounterRegion + p->part_bytes;
     return GQA_OK;
 }
@@ -250,6 +252,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.T = shape->T;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.deferred = plan.deferred;
+    a.slot_rows = plan.slot_rows;
 
     hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

@@ -24,7 +24,7 @@ enum class Path : int { VALU = 1, MFMA = 2, MFMA_QK = 3 };
 
 // Floats in one partial slot: rb rows of d values, then the rows'
 // log2-sum-exp padded to a multiple of 16 (slots stay 64-byte aligned).
-__host__ __device__ constexpr int slot_floats(int rb, int d) { return rb * d + (rb > 16 ? rb : 16); }
+__host__ __device__ constexpr int slot_floats(int rb, int d) { return rb * d + (((rb > 16 ? rb : 16) + 15) & ~15); }
 
 struct Plan {
     Path path;
@@ -35,6 +35,7 @@ struct Plan {
     int n_rb;           // row blocks per (b, g)
     int64_t grid;       // workgroups (one wave each) P
     int deferred;       // 1: split segments are merged by a second, parallel kernel
+    int slot_rows;      // matrix-core path: rows per partial slot, min(row_block, R)
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };
@@ -50,6 +51,7 @@ struct Args {
     int B, H, G, sq, T;
     float scale_log2;   // scale * log2(e): scores kept in base-2 exponent units
     int deferred;       // leave every split segment's partials for the combine kernel
+    int slot_rows;      // matrix-core path: query rows per partial slot
 };
 
 // Queue the decode kernel on stream.

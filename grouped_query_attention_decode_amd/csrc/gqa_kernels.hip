@@ -295,6 +295,7 @@ struct Sched {
     long long total;     // W
     long long first_b;   // first sequence this workgroup touches
     long long first_e;   // units before that sequence
+    int P;               // workgroups that share the work: min(grid, W), so none is empty
 };
 
 // W = units_per_seq * sum_b clamp(L_b); then the first sequence whose units
@@ -312,6 +313,10 @@ __device__ __forceinline__ Sched schedule_wave(const Args& a, int units_per_seq,
     s.total = tot * units_per_seq;
     s.first_b = a.B;
     s.first_e = s.total;
+    // with fewer units than workgroups, the first W take one unit each (an
+    // empty workgroup inside a segment's range would never arrive)
+    if (s.total > 0 && s.total < P) P = (int)s.total;
+    s.P = P;
     const long long A = wg_start(s.total, P, p);
     long long carry = 0;
     for (int b0 = 0; b0 < a.B && s.total > 0; b0 += kWave) {
@@ -840,10 +845,10 @@ __global__ void __launch_bounds__(kWave)
 decode_valu(const Args a, const int R, const int n_rb)
 {
     __shared__ ValuShared<FMT, D, RB> sm;
-    const int P = gridDim.x;
     const int p = blockIdx.x;
-    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
-    zero_empty_sequences<D>(a, P, p);
+    const Sched sched = schedule_wave(a, a.G * n_rb, gridDim.x, p);
+    zero_empty_sequences<D>(a, gridDim.x, p);
+    const int P = sched.P;
     const long long W = sched.total;
     if (W == 0) return;
     for_each_piece(a, sched, n_rb, P, p,
@@ -910,6 +915,20 @@ struct Piece {
 struct PieceIter {
     long long A, E, Eb, k;
     int b, units, n_rb;
+
+    // the units [A_, E_) of one chunk; fb / fe: first sequence reaching past
+    // A_ and the units before it
+    __device__ __forceinline__ void init_range(long long A_, long long E_, int fb, long long fe, int G,
+                                               int n_rb_)
+    {
+        A = A_;
+        E = E_;
+        Eb = fe;
+        b = fb;
+        k = -1;
+        n_rb = n_rb_;
+        units = G * n_rb_;
+    }
 
     __device__ __forceinline__ void init(const Sched& sh, int G, int n_rb_, int P, int p)
     {
@@ -1132,11 +1151,11 @@ decode_mqk(const Args a, const int R, const int n_rb)
     constexpr int LPT = D / EPL;
     constexpr int NAK = RB * EPL / (kWave / LPT);
     __shared__ MqkShared sm;
-    const int P = gridDim.x;
     const int p = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
-    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
-    zero_empty_sequences<D>(a, P, p);
+    const Sched sched = schedule_wave(a, a.G * n_rb, gridDim.x, p);
+    zero_empty_sequences<D>(a, gridDim.x, p);
+    const int P = sched.P;
     const long long W = sched.total;
     if (W == 0) return;
     const int lbase = (int)sched.first_b;
@@ -1230,6 +1249,95 @@ __device__ __forceinline__ float sum_x32(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---------------------------------------------------------------------------
+// Work split of the matrix-core pass: the W work units (cache rows of all
+// segments, in order) are cut into P chunks with fixed boundaries, chunk
+// c = [c W / P, (c + 1) W / P) taken by workgroup c; with fewer units than
+// workgroups, only the first W workgroups take one unit each, so no chunk
+// is empty (a merge waits for every chunk between a segment's first and
+// last).  A piece is a chunk's part of one segment; its partial lives in a
+// slot of the chunk, and merges go in chunk order.
+//
+// (A guided deal -- most of each share static, the rest in small chunks
+// handed out by a global counter -- was measured slower on every workload:
+// thousands of device-scope atomics on one address serialise.)
+// ---------------------------------------------------------------------------
+struct ChunkMap {
+    long long W;
+    int P;
+
+    __device__ __forceinline__ long long start(int c) const { return (long long)c * W / P; }
+    // the chunk holding unit x, 0 <= x < W
+    __device__ __forceinline__ int of(long long x) const { return (int)(((x + 1) * P - 1) / W); }
+};
+
+__device__ __forceinline__ ChunkMap make_map(long long W, int P)
+{
+    ChunkMap m;
+    m.W = W;
+    m.P = W < P ? (int)W : P;
+    return m;
+}
+
+// Partial slots of the matrix-core pass: two per chunk (slot 0 for the
+// segment holding the chunk's first unit, slot 1 for the one that starts
+// inside it and runs past its end), each a.slot_rows rows of D values, then
+// their log2-sum-exp.
+struct MSlots {
+    int stride;   // floats per slot
+    int lse;      // offset of the log2-sum-exp values in a slot
+    __device__ __forceinline__ int base(int c, int which) const { return (2 * c + which) * stride; }
+};
+
+template <int D>
+__device__ __forceinline__ MSlots mslots(const Args& a)
+{
+    MSlots m;
+    m.lse = a.slot_rows * D;
+    m.stride = slot_floats(a.slot_rows, D);
+    return m;
+}
+
+__device__ __forceinline__ int lens_at(const Args& a, const int* lens, int b)
+{
+    return b < kLensWindow ? lens[b] : clamp_len(a.seq_lens, b, a.T);
+}
+
+// Sum of the clamped lengths (every lane gets it).
+__device__ __forceinline__ long long total_rows(const Args& a, const int* lens)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    long long tot = 0;
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
+        const int b = b0 + lane;
+        tot += wave_sum_u32(b < a.B ? (uint32_t)lens_at(a, lens, b) : 0u);
+    }
+    return tot;
+}
+
+// First sequence whose units reach past unit x, and the units before it.
+__device__ __forceinline__ void locate(const Args& a, const int* lens, int units, long long x, int& first_b,
+                                       long long& first_e)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    long long carry = 0;
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
+        const int b = b0 + lane;
+        const uint32_t L = b < a.B ? (uint32_t)lens_at(a, lens, b) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(L, lane);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
+        if (hit) {
+            const int f = __builtin_ctzll(hit);
+            first_b = b0 + f;
+            first_e = (carry + __shfl(incl - L, f)) * units;
+            return;
+        }
+        carry += __shfl(incl, kWave - 1);
+    }
+    first_b = a.B;
+    first_e = carry * units;
+}
+
 // One piece of segment (b, g, rb) -- cache rows [ta, tb) for the RB = 16 NB
 // query rows RB rb .. RB rb + RB - 1 -- streamed in 16-row tiles with the
 // next tiles' loads in flight; then written out, or left as a partial
@@ -1237,7 +1345,7 @@ __device__ __forceinline__ float sum_x32(float x)
 // blocks share every K/V tile: it is read once for all of them.
 template <int D, int NB>
 __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
-                                          long long W, int P, int p, Pending* pd)
+                                          const ChunkMap& cm, int chunk, Pending* pd)
 {
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
@@ -1387,8 +1495,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         inv[nb] = l > 0.0f ? 1.0f / l : 0.0f;
         lse[nb] = l > 0.0f ? m_run[nb] + __log2f(l) : -INFINITY;
     }
-    const int p_first = wg_of(pc.off, W, P);
-    const int npieces = wg_of(pc.off + pc.L - 1, W, P) - p_first + 1;
+    const int c_first = cm.of(pc.off);
+    const int npieces = cm.of(pc.off + pc.L - 1) - c_first + 1;
     if (npieces == 1) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -1400,7 +1508,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         return false;
     }
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
-    const int mine = slot_base<D, RB>(p, pc.off, W, P);
+    const MSlots ms = mslots<D>(a);
+    const int mine = ms.base(chunk, cm.start(chunk) >= pc.off ? 0 : 1);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         if (!live[nb]) continue;
@@ -1411,10 +1520,10 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             const float ov[4] = {o[0], o[1], o[2], o[3]};
             store4_coherent(part, mine + r * D + 16 * c + 4 * kg, ov);
         }
-        if (kg == 0) store_coherent(part, mine + RB * D + r, lse[nb]);
+        if (kg == 0) store_coherent(part, mine + ms.lse + r, lse[nb]);
     }
     pd->seg = (pc.b * a.G + pc.g) * n_rb + pc.rb;
-    pd->p_first = p_first;
+    pd->p_first = c_first;
     pd->npieces = npieces;
     pd->off = pc.off;
     pd->qrow0 = qrow0;
@@ -1426,12 +1535,13 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 // values, then the rows' log2-sum-exp), in piece order.  The live rows are
 // spread over the wave, LPR lanes per row, NF float4 of the row per lane;
 // KB pieces are loaded at a time, all their loads in flight together.
-template <int D, int RB, int NF, int KB>
+template <int D, int NF, int KB>
 __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, int lane, int r0, int rows,
-                                             long long W, int P)
+                                             const ChunkMap& cm)
 {
     constexpr int LPR = D / (4 * NF);
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const MSlots ms = mslots<D>(a);
     const int i = lane / LPR;
     const int ic = r0 + min(i, rows - 1);
     const int e0 = (lane % LPR) * 4 * NF;
@@ -1441,13 +1551,14 @@ __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, i
     for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int q = 0; q < 4; ++q) num[f][q] = 0.0f;
-    const bool tail1 = wg_start(W, P, pd.p_first) < pd.off;
+    const bool tail1 = cm.start(pd.p_first) < pd.off;
     for (int k0 = 0; k0 < pd.npieces; k0 += KB) {
         float lse[KB], ov[KB][NF][4];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
-            const int base = piece_slot<D, RB>(pd.p_first, min(k0 + kk, pd.npieces - 1), tail1);
-            lse[kk] = load_coherent(part, base + RB * D + ic);
+            const int k = min(k0 + kk, pd.npieces - 1);
+            const int base = ms.base(pd.p_first + k, k == 0 && tail1 ? 1 : 0);
+            lse[kk] = load_coherent(part, base + ms.lse + ic);
 #pragma unroll
             for (int f = 0; f < NF; ++f) load4_coherent(part, base + ic * D + e0 + 4 * f, ov[kk][f]);
         }
@@ -1477,8 +1588,8 @@ __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, i
 // of live rows), and resets the counter.  The caller has waited for its own
 // partial stores.
 template <int D, int RB>
-__device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pending& pd, int lane, int R, long long W,
-                                                     int P)
+__device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pending& pd, int lane, int R,
+                                                     const ChunkMap& cm)
 {
     int old = 0;
     if (lane == 0)
@@ -1491,13 +1602,13 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
         // lanes per row: 64 / (rows rounded up to a power of two), at most D / 4;
         // about 32 to 48 loads of a batch in flight per lane
         if (rows > 8)
-            merge_pieces<D, RB, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, W, P);
+            merge_pieces<D, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, cm);
         else if (rows > 4)
-            merge_pieces<D, RB, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, W, P);
+            merge_pieces<D, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, cm);
         else if (rows > 2 || D == 64)
-            merge_pieces<D, RB, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, W, P);
+            merge_pieces<D, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, cm);
         else
-            merge_pieces<D, RB, 1, 16>(a, pd, lane, r0, rows, W, P);
+            merge_pieces<D, 1, 16>(a, pd, lane, r0, rows, cm);
     }
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1510,29 +1621,33 @@ decode_mfa(const Args a, const int R, const int n_rb)
     const int P = gridDim.x;
     const int p = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
-    const Sched sched = schedule_wave(a, a.G * n_rb, P, p);
     zero_empty_sequences<D>(a, P, p);
-    const long long W = sched.total;
-    if (W == 0) return;
-    const int lbase = (int)sched.first_b;
-    for (int i = lane; i < kLensWindow; i += kWave)
-        sm.lens[i] = lbase + i < a.B ? clamp_len(a.seq_lens, lbase + i, a.T) : 0;
+    for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
-
+    const int units = a.G * n_rb;
+    const long long W = total_rows(a, sm.lens) * units;
+    if (W == 0) return;
+    const ChunkMap cm = make_map(W, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer units than workgroups
+    const long long A = cm.start(chunk), E = cm.start(chunk + 1);
+    int fb;
+    long long fe;
+    locate(a, sm.lens, units, A, fb, fe);
     PieceIter it;
-    it.init(sched, a.G, n_rb, P, p);
+    it.init_range(A, E, fb, fe, a.G, n_rb);
     Piece pc;
-    while (it.next(a, sm.lens, lbase, pc)) {
+    while (it.next(a, sm.lens, 0, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB>(a, sm, R, n_rb, pc, W, P, p, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
-            arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, W, P);
+            arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
     }
 }
 
 // Combine pass for a deferred plan: one wave per (segment, query row) of a
-// split segment merges the row's partials, in piece order (the same
+// split segment merges the row's partials, in chunk order (the same
 // log2-sum-exp merge as the in-kernel one).  Lane l holds elements
 // 4 l .. 4 l + 3 of the row; KB pieces' loads are in flight together.
 template <int D, int RB>
@@ -1559,13 +1674,14 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
         before += wave_sum_u32(bb < b ? Lb : 0u);
     }
     const long long units = (long long)a.G * n_rb;
-    const long long W = tot * units;
+    const ChunkMap cm = make_map(tot * units, P);
     const long long off = before * units + ((long long)g * n_rb + rb) * L;
-    const int p_first = wg_of(off, W, P);
-    const int npieces = wg_of(off + L - 1, W, P) - p_first + 1;
+    const int c_first = cm.of(off);
+    const int npieces = cm.of(off + L - 1) - c_first + 1;
     if (npieces == 1) return;                 // written by its piece
-    const bool tail1 = wg_start(W, P, p_first) < off;
+    const bool tail1 = cm.start(c_first) < off;
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const MSlots ms = mslots<D>(a);
     const int e = 4 * min(lane, D / 4 - 1);
     float M = -INFINITY, den = 0.0f;
     float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1573,8 +1689,9 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
         float lse[KB], ov[KB][4];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
-            const int base = piece_slot<D, RB>(p_first, min(k0 + kk, npieces - 1), tail1);
-            lse[kk] = load_coherent(part, base + RB * D + r);
+            const int k = min(k0 + kk, npieces - 1);
+            const int base = ms.base(c_first + k, k == 0 && tail1 ? 1 : 0);
+            lse[kk] = load_coherent(part, base + ms.lse + r);
             load4_coherent(part, base + r * D + e, ov[kk]);
         }
 #pragma unroll

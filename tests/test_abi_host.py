@@ -61,10 +61,10 @@ def test_plan_of_batched_gqa8(lib):
     assert p["row_blocks"] == 1 and p["row_block"] == 16
     P = p["workgroups"]
     assert 1 <= P <= 4096
-    # workspace: a fixed 1 MiB counter region, then two partial slots per
-    # workgroup (16 query rows x 128 values + 16 lse floats) -- far below a
-    # repeated K/V copy (n_rep = 4 times the cache)
-    assert p["workspace_bytes"] == (1 << 20) + _round256(P * 2 * (16 * 128 + 16) * 4)
+    # a fixed 1 MiB counter region, then two partial slots per workgroup, a
+    # slot holding the 4 live query rows x 128 values + 16 lse floats -- far
+    # below a repeated K/V copy (n_rep = 4 times the cache)
+    assert p["workspace_bytes"] == (1 << 20) + _round256(P * 2 * (4 * 128 + 16) * 4)
     kv_bytes = 2 * 32 * 8 * 4096 * 128 * 2
     assert p["workspace_bytes"] < kv_bytes // 20
     assert gqa.workspace_bytes(_shape(B=32)) == p["workspace_bytes"]
@@ -107,8 +107,11 @@ def test_plan_matrix_path_row_blocks(lib):
         p = gqa.plan(_shape(H=H, G=G, sq=sq))
         assert p["path"] == gqa.PATH_MFMA
         assert (p["rows_per_group"], p["row_block"], p["row_blocks"]) == (rows, rb, nrb), (H, G, sq)
-        # slots: rb rows of 128 values, then max(rb, 16) log-sum-exp floats
-        assert p["workspace_bytes"] == (1 << 20) + _round256(p["workgroups"] * 2 * (rb * 128 + max(rb, 16)) * 4)
+        # slots (two per workgroup): min(rb, rows) rows of 128 values, then
+        # their log-sum-exp floats padded to a multiple of 16 (at least 16)
+        sr = min(rb, rows)
+        lse = (max(sr, 16) + 15) // 16 * 16
+        assert p["workspace_bytes"] == (1 << 20) + _round256(p["workgroups"] * 2 * (sr * 128 + lse) * 4)
 
 
 def test_plan_merge_mode(lib):
@@ -126,6 +129,7 @@ def test_plan_merge_mode(lib):
     with pytest.raises(gqa.GqaError) as ei:
         gqa.plan(_shape(), merge=3)
     assert ei.value.status == gqa.GQA_ERR_INVALID_ARG
+
     # the combine flag does not change the workspace
     assert gqa.plan(mqa)["workspace_bytes"] == gqa.plan(mqa, merge=gqa.MERGE_IN_KERNEL)["workspace_bytes"]
 

@@ -204,18 +204,29 @@ def test_split_invariance_and_determinism(gqa, orc, dt, path_name):
 @pytest.mark.parametrize("H,G,sq,D", [(32, 8, 1, 128), (32, 1, 1, 128), (32, 1, 2, 64), (24, 1, 2, 128)])
 def test_merge_modes_match_oracle(gqa, orc, H, G, sq, D):
     """The in-kernel merge and the combine kernel both give the oracle's
-    result at several splits, and each is deterministic."""
+    result at several splits, and each gives the same bits on a second call."""
     x = gi.make_custom(4, H, G, D, 777, sq, dtype="bf16", seed=300 + H + G + sq,
                        seq_lens=[777, 3, 400, 129])
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
     xc = _to(x, "cuda")
     for P in (5, 64, 300):
-        outs = {}
         for m in (gqa.MERGE_IN_KERNEL, gqa.MERGE_COMBINE):
-            o = _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=m)
+            kw = dict(path=gqa.PATH_MFMA, workgroups=P, merge=m)
+            o = _run(gqa, xc, **kw)
             _compare(o, want, TOL["bf16"], "P=%d merge=%d" % (P, m))
-            assert torch.equal(o, _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=m))
-            outs[m] = o
+            assert torch.equal(o, _run(gqa, xc, **kw))
+
+
+@pytest.mark.parametrize("dt,path_name", [("f32", "valu"), ("bf16", "mfma"), ("bf16", "mfma_qk")])
+def test_more_workgroups_than_cache_rows(gqa, orc, dt, path_name):
+    """A grid far larger than the work (here 10 units for 64 or 500
+    workgroups) still gives every split segment all of its pieces."""
+    path = {"valu": gqa.PATH_VALU, "mfma": gqa.PATH_MFMA, "mfma_qk": gqa.PATH_MFMA_QK}[path_name]
+    x = gi.make_custom(2, 8, 2, 64, 64, 1, dtype=dt, seed=17, seq_lens=[3, 2])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"])
+    xc = _to(x, "cuda")
+    for P in (7, 64, 500):
+        _compare(_run(gqa, xc, path=path, workgroups=P), want, TOL[dt], "%s P=%d" % (path_name, P))
 
 
 def test_explicit_workspace_matches_library_workspace(gqa):
