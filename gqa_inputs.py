@@ -87,6 +87,11 @@ WORKLOADS = {
     "sweep_b16_h32_g1_d128_t16384_sq2": Workload(
         "sweep_b16_h32_g1_d128_t16384_sq2", B=16, H=32, G=1, D=128,
         T=16384, sq=2, dtype="bf16", seed=1008),
+    # 64 new query tokens per sequence (causal among them) on a ragged cache:
+    # 256 query rows share each KV head
+    "multitoken_b8_h32_g8_d128_t4096_sq64": Workload(
+        "multitoken_b8_h32_g8_d128_t4096_sq64", B=8, H=32, G=8, D=128, T=4096,
+        sq=64, dtype="bf16", seed=1009, ragged=(1024, 4096)),
 }
 
 # The workload the benchmark times: batched GQA-8 decode at B=32, T=4096.

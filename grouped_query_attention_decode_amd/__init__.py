@@ -11,6 +11,13 @@ q [B,H,sq,D], k_cache / v_cache [B,G,T,D] (contiguous, on one GPU, both
 float32 or both bfloat16), seq_lens [B] int32 on the same GPU or None,
 out [B,H,sq,D] float32.  Query head h reads KV head h // (H/G)
 ("GQA (Grouped-Query Attention) 분석", section "Grouped broadcast").
+
+    out = decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens)   # bf16
+    out = decode_paged(q, k_pages, v_pages, block_table, seq_lens)     # bf16
+
+decode_append stores the sq new tokens' K/V (k_new / v_new [B,G,sq,D]) at
+cache rows L-sq .. L-1 and attends in the same pass; decode_paged reads a
+page pool [num_pages, G, page_size, D] through block_table [B, max_pages].
 """
 from __future__ import annotations
 
@@ -19,7 +26,8 @@ import math
 import os
 import threading
 
-__all__ = ["decode", "plan", "workspace_bytes", "version", "library_path",
+__all__ = ["decode", "decode_append", "decode_paged", "plan", "workspace_bytes",
+           "paged_workspace_bytes", "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
            "EXPORTED_SYMBOLS"]
@@ -34,7 +42,8 @@ MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",
-                    "gqa_decode_ex", "gqa_plan", "gqa_last_error", "gqa_version")
+                    "gqa_decode_ex", "gqa_decode_append", "gqa_paged_workspace_bytes",
+                    "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
 
 class GqaError(RuntimeError):
@@ -46,6 +55,14 @@ class GqaError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
                 ("sq", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class PagedShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("sq", ctypes.c_int32), ("D", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32)]
 
@@ -96,6 +113,15 @@ def load_library():
         lib.gqa_decode_ex.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_ex.restype = ctypes.c_int
+        lib.gqa_decode_append.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
+                                          ctypes.c_size_t, ctypes.POINTER(Options), vp]
+        lib.gqa_decode_append.restype = ctypes.c_int
+        psp = ctypes.POINTER(PagedShape)
+        lib.gqa_paged_workspace_bytes.argtypes = [psp]
+        lib.gqa_paged_workspace_bytes.restype = ctypes.c_size_t
+        lib.gqa_decode_paged.argtypes = [psp, vp, vp, vp, i32p, i32p, ctypes.c_float, vp, vp,
+                                         ctypes.c_size_t, ctypes.POINTER(Options), vp]
+        lib.gqa_decode_paged.restype = ctypes.c_int
         lib.gqa_plan.argtypes = [sp, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
         lib.gqa_plan.restype = ctypes.c_int
         lib.gqa_last_error.argtypes = []
@@ -213,5 +239,112 @@ def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
             seq_lens.data_ptr() if seq_lens is not None else None,
             ctypes.c_float(scale), out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len),
             ctypes.byref(opts), sptr)
+    _check(st)
+    return out
+
+
+def _common_checks(q, tensors, seq_lens, out):
+    import torch
+    dev = q.device
+    for name, t in tensors:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("%s must be a GPU tensor on q's device" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or seq_lens.device != dev or \
+                seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 [B] tensor on q's device")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    elif out.shape != q.shape or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,H,sq,D] tensor on q's device")
+    return out
+
+
+def _ws(workspace, dev):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or workspace.device != dev:
+        raise ValueError("workspace must be on q's device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
+                  path=PATH_AUTO, workgroups=0, merge=0, workspace=None, stream=None):
+    """Store the new tokens' K/V (k_new / v_new [B,G,sq,D]) at cache rows
+    L-sq .. L-1 (L = seq_lens[b], which counts them) and return the decode
+    attention over rows 0 .. L-1 -- one pass (bf16)."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H,sq,D] and k_cache/v_cache [B,G,T,D]")
+    B, H, sq, D = q.shape
+    G = k_cache.shape[1]
+    if k_new.shape != (B, G, sq, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [B,G,sq,D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_new, v_new and the caches must share a dtype")
+    out = _common_checks(q, (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                             ("v_cache", v_cache)), seq_lens, out)
+    dev = q.device
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    shape = shape_of(q, k_cache, out.dtype)
+    stream = torch.cuda.current_stream(dev) if stream is None else stream
+    ws_ptr, ws_len = _ws(workspace, dev)
+    opts = _options(path, workgroups, merge)
+    with torch.cuda.device(dev):
+        st = lib.gqa_decode_append(
+            ctypes.byref(shape), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr() if seq_lens is not None else None, ctypes.c_float(scale),
+            out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len), ctypes.byref(opts),
+            ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+    return out
+
+
+def paged_shape_of(q, k_pages, block_table, out_dtype=None) -> PagedShape:
+    import torch
+    B, H, sq, D = q.shape
+    num_pages, G, page_size, Dk = k_pages.shape
+    if Dk != D or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("expected k_pages [num_pages,G,page_size,D] and block_table [B,max_pages]")
+    return PagedShape(B, H, G, sq, D, page_size, num_pages, block_table.shape[1],
+                      _dtype_code(q.dtype), _dtype_code(k_pages.dtype),
+                      _dtype_code(out_dtype or torch.float32))
+
+
+def paged_workspace_bytes(shape: PagedShape) -> int:
+    return int(load_library().gqa_paged_workspace_bytes(ctypes.byref(shape)))
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens=None, scale=None, out=None, *,
+                 path=PATH_AUTO, workgroups=0, merge=0, workspace=None, stream=None):
+    """Decode attention over a paged cache: k_pages / v_pages
+    [num_pages, G, page_size, D], block_table [B, max_pages] int32 (row t of
+    sequence b is row t % page_size of page block_table[b, t // page_size])."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("expected q [B,H,sq,D] and k_pages/v_pages [num_pages,G,page_size,D]")
+    if v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages must share a dtype")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    out = _common_checks(q, (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                             ("block_table", block_table)), seq_lens, out)
+    dev = q.device
+    scale = 1.0 / math.sqrt(q.shape[3]) if scale is None else scale
+    shape = paged_shape_of(q, k_pages, block_table, out.dtype)
+    stream = torch.cuda.current_stream(dev) if stream is None else stream
+    ws_ptr, ws_len = _ws(workspace, dev)
+    opts = _options(path, workgroups, merge)
+    with torch.cuda.device(dev):
+        st = lib.gqa_decode_paged(
+            ctypes.byref(shape), q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+            block_table.data_ptr(), seq_lens.data_ptr() if seq_lens is not None else None,
+            ctypes.c_float(scale), out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len),
+            ctypes.byref(opts), ctypes.c_void_p(stream.cuda_stream))
     _check(st)
     return out

@@ -106,6 +106,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     else
         p->path = gqa::Path::MFMA;
     p->kv_bf16 = bf16 ? 1 : 0;
+    p->src = 0;
     p->D = s->D;
     p->R = R;
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
@@ -215,18 +216,33 @@ gqa_status_t library_workspace(size_t need, void** out)
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Where the K/V rows come from, beyond the plain [B, G, T, D] caches.
+struct Source {
+    int src = 0;                       // gqa kernel source kind (0 cache, 1 append, 2 paged)
+    const void* k_new = nullptr;       // append: [B, G, sq, D]
+    const void* v_new = nullptr;
+    const int32_t* block_table = nullptr;  // paged: [B, max_pages]
+    int page_shift = 0, num_pages = 0, max_pages = 0;
+};
+
 gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const void* v,
                  const int32_t* seq_lens, float scale, void* out, void* workspace, size_t ws_bytes,
-                 bool library_ws, const gqa_options_t* opts, void* stream)
+                 bool library_ws, const gqa_options_t* opts, void* stream, const Source& srcx = Source())
 {
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan);
     if (st != GQA_OK) return st;
+    if (srcx.src != 0 && plan.path != gqa::Path::MFMA)
+        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 matrix-core path");
+    plan.src = srcx.src;
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale must be finite");
     if (shape->B == 0) return ok();
     if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be non-NULL");
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
         return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (srcx.src == 1 && (!srcx.k_new || !srcx.v_new || misaligned(srcx.k_new) || misaligned(srcx.v_new)))
+        return fail(GQA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL and 16-byte aligned");
+    if (srcx.src == 2 && !srcx.block_table) return fail(GQA_ERR_INVALID_ARG, "block_table must be non-NULL");
     if (library_ws) {
         st = library_workspace(plan.ws_bytes, &workspace);
         if (st != GQA_OK) return st;
@@ -253,6 +269,12 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.scale_log2 = scale * 1.4426950408889634f;
     a.deferred = plan.deferred;
     a.slot_rows = plan.slot_rows;
+    a.k_new = srcx.k_new;
+    a.v_new = srcx.v_new;
+    a.block_table = srcx.block_table;
+    a.page_shift = srcx.page_shift;
+    a.num_pages = srcx.num_pages;
+    a.max_pages = srcx.max_pages;
 
     hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -292,6 +314,73 @@ gqa_status_t gqa_decode_ex(const gqa_shape_t* shape, const void* q, const void* 
     const bool lib_ws = workspace == nullptr && ws_bytes == 0;
     return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts,
                stream);
+}
+
+gqa_status_t gqa_decode_append(const gqa_shape_t* shape, const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                               void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
+{
+    Source sx;
+    sx.src = 1;
+    sx.k_new = k_new;
+    sx.v_new = v_new;
+    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
+}
+
+// The contiguous shape a paged one plans as: T = page_size * max_pages.
+static gqa_status_t paged_as_shape(const gqa_paged_shape_t* ps, gqa_shape_t* s, int* shift)
+{
+    if (!ps) return fail(GQA_ERR_INVALID_ARG, "shape is NULL");
+    if (ps->page_size < 16 || ps->page_size > (1 << 16) || (ps->page_size & (ps->page_size - 1)))
+        return fail(GQA_ERR_INVALID_ARG, "page_size (%d) must be a power of two in [16, 65536]", ps->page_size);
+    if (ps->num_pages <= 0 || ps->max_pages <= 0)
+        return fail(GQA_ERR_INVALID_ARG, "num_pages (%d) and max_pages (%d) must be positive", ps->num_pages,
+                    ps->max_pages);
+    const int64_t T = (int64_t)ps->page_size * ps->max_pages;
+    if (T >= ((int64_t)1 << 30)) return fail(GQA_ERR_INVALID_ARG, "page_size * max_pages too large");
+    if ((int64_t)ps->num_pages * ps->G * ps->page_size * (ps->D > 0 ? ps->D : 1) >= ((int64_t)1 << 40))
+        return fail(GQA_ERR_INVALID_ARG, "page pool too large");
+    s->B = ps->B;
+    s->H = ps->H;
+    s->G = ps->G;
+    s->sq = ps->sq;
+    s->T = (int32_t)T;
+    s->D = ps->D;
+    s->q_dtype = ps->q_dtype;
+    s->kv_dtype = ps->kv_dtype;
+    s->out_dtype = ps->out_dtype;
+    int sh = 0;
+    while ((1 << sh) < ps->page_size) ++sh;
+    *shift = sh;
+    return GQA_OK;
+}
+
+size_t gqa_paged_workspace_bytes(const gqa_paged_shape_t* shape)
+{
+    gqa_shape_t s;
+    int sh = 0;
+    if (paged_as_shape(shape, &s, &sh) != GQA_OK) return 0;
+    gqa::Plan plan;
+    if (make_plan(&s, nullptr, &plan) != GQA_OK) return 0;
+    return plan.ws_bytes;
+}
+
+gqa_status_t gqa_decode_paged(const gqa_paged_shape_t* shape, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                              float scale, void* out, void* workspace, size_t ws_bytes,
+                              const gqa_options_t* opts, void* stream)
+{
+    gqa_shape_t s;
+    Source sx;
+    gqa_status_t st = paged_as_shape(shape, &s, &sx.page_shift);
+    if (st != GQA_OK) return st;
+    sx.src = 2;
+    sx.block_table = block_table;
+    sx.num_pages = shape->num_pages;
+    sx.max_pages = shape->max_pages;
+    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
+    return run(&s, q, k_pages, v_pages, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
 }
 
 gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_plan_t* plan)

@@ -36,6 +36,7 @@ struct Plan {
     int64_t grid;       // workgroups (one wave each) P
     int deferred;       // 1: split segments are merged by a second, parallel kernel
     int slot_rows;      // matrix-core path: rows per partial slot, min(row_block, R)
+    int src;            // matrix-core path: 0 cache, 1 cache + appended tokens, 2 paged cache
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };
@@ -52,6 +53,15 @@ struct Args {
     float scale_log2;   // scale * log2(e): scores kept in base-2 exponent units
     int deferred;       // leave every split segment's partials for the combine kernel
     int slot_rows;      // matrix-core path: query rows per partial slot
+    // cache with appended tokens: the sq new rows of every (b, g), [B, G, sq, D]
+    const void* k_new;
+    const void* v_new;
+    // paged cache: k / v are page pools [num_pages, G, 1 << page_shift, D];
+    // block_table [B, max_pages] holds each sequence's pages in order
+    const int32_t* block_table;
+    int page_shift;
+    int num_pages;
+    int max_pages;
 };
 
 // Queue the decode kernel on stream.

@@ -1207,11 +1207,19 @@ constexpr float kSlack = 8.0f;
 template <int NB>
 constexpr int mfa_buffers() { return NB >= 4 ? 2 : 3; }
 
+constexpr int kPageWindow = 1024;        // block-table entries a wave keeps in LDS (paged cache)
+
+// Where the matrix-core pass reads K/V rows from.
+constexpr int kSrcCache = 0;    // contiguous [B, G, T, D] cache
+constexpr int kSrcAppend = 1;   // the cache, the last sq rows taken from (and written with) new tokens
+constexpr int kSrcPaged = 2;    // page pool [num_pages, G, page_size, D] and a block table
+
 template <int D>
 struct MfaShared {
     static constexpr int SE = D + 16;   // LDS row stride (bf16): the four row groups of a read hit distinct banks
     alignas(16) uint16_t vt[16 * SE];   // V tile, row-major
-    int lens[kLensWindow];              // clamped seq_lens[first_b + i]
+    int lens[kLensWindow];              // clamped seq_lens[i]
+    int pages[kPageWindow];             // paged cache: physical pages of the current row window
 };
 
 // Two floats to packed bf16 (round to nearest even), element 0 in the low half.
@@ -1343,7 +1351,7 @@ __device__ __forceinline__ void locate(const Args& a, const int* lens, int units
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
-template <int D, int NB>
+template <int D, int NB, int SRC>
 __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
@@ -1386,23 +1394,44 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[nb][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // Where cache row t of (b, g) lives (byte address of its element 0):
+    //   kSrcCache  : the [B, G, T, D] cache;
+    //   kSrcAppend : rows t >= L - sq are the new tokens, read from
+    //                k_new / v_new [B, G, sq, D] (and written into the cache);
+    //   kSrcPaged  : page block_table[b][t >> page_shift] of the page pool
+    //                [num_pages, G, page_size, D], row t & (page_size - 1).
     const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
-    const char* kbase = static_cast<const char*>(a.k) + (slab + 8 * kg) * 2;
-    const char* vbase = static_cast<const char*>(a.v) + slab * 2;
+    const int la = pc.L - a.sq;
+    const int64_t nslab = ((int64_t)pc.b * a.G + pc.g) * a.sq * D;
+    int wpage0 = 0;                      // paged: first page of the LDS window
+    auto row_addr = [&](const void* base, const void* fresh, int t) -> const char* {
+        if constexpr (SRC == kSrcPaged) {
+            const int pg = min(max(sm.pages[(t >> a.page_shift) - wpage0], 0), a.num_pages - 1);
+            const int64_t r = (((int64_t)pg * a.G + pc.g) << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+            return static_cast<const char*>(base) + r * D * 2;
+        } else if constexpr (SRC == kSrcAppend) {
+            return t >= la ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * 2
+                           : static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
+        } else {
+            (void)fresh;
+            return static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
+        }
+    };
+    int tend = tb;                       // end of the current row window
 
-    // Rows past the piece's end re-read row tb - 1 (valid): their weights
-    // are exactly 0, so no row at or beyond tb is read and no branch guards
-    // the loads.  K: lane (kg, col) loads row col, elements 8 kg + 32 s ..;
-    // V: chunk c = lane + 64 j is row c / CPR, elements 8 (c % CPR) ..
+    // Rows past the window's end re-read its last row (valid): their weights
+    // are exactly 0, so no row at or beyond the end is read and no branch
+    // guards the loads.  K: lane (kg, col) loads row col, elements
+    // 8 kg + 32 s ..; V: chunk c = lane + 64 j is row c / CPR, elements
+    // 8 (c % CPR) ..
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
-        const int tk = min(t0 + col, tb - 1);
+        const char* kr = row_addr(a.k, a.k_new, min(t0 + col, tend - 1)) + 16 * kg;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) kk[s] = load16_stream(kbase + ((int64_t)tk * D + 32 * s) * 2);
+        for (int s = 0; s < NK; ++s) kk[s] = load16_stream(kr + 64 * s);
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
-            const int tv = min(t0 + c / CPR, tb - 1);
-            vv[j] = load16_stream(vbase + ((int64_t)tv * D + (c % CPR) * 8) * 2);
+            vv[j] = load16_stream(row_addr(a.v, a.v_new, min(t0 + c / CPR, tend - 1)) + (c % CPR) * 16);
         }
     };
 
@@ -1411,6 +1440,25 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
             *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+        }
+        if constexpr (SRC == kSrcAppend) {
+            // the first row block's pieces store the new tokens' rows into the cache
+            if (pc.rb == 0) {
+                const int tk = t0 + col;
+                if (tk >= la && tk < tend) {
+                    char* kr = static_cast<char*>(const_cast<void*>(a.k)) + (slab + (int64_t)tk * D) * 2 + 16 * kg;
+#pragma unroll
+                    for (int s = 0; s < NK; ++s) *reinterpret_cast<uint4*>(kr + 64 * s) = kk[s];
+                }
+#pragma unroll
+                for (int j = 0; j < NLV; ++j) {
+                    const int c = lane + kWave * j;
+                    const int tv = t0 + c / CPR;
+                    if (tv >= la && tv < tend)
+                        *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) +
+                                                  (slab + (int64_t)tv * D) * 2 + (c % CPR) * 16) = vv[j];
+                }
+            }
         }
         s16x4_t ph[NB], pl[NB];
 #pragma unroll
@@ -1425,7 +1473,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int t = t0 + 4 * kg + jj;
-                sc[jj] = (t < tb && t <= last[nb]) ? s4[jj] * a.scale_log2 : -INFINITY;
+                sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * a.scale_log2 : -INFINITY;
                 mx = fmaxf(mx, sc[jj]);
             }
             mx = max_x32(max_x16(mx));
@@ -1467,12 +1515,24 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 
     // NBUF register buffers in rotation, NBUF - 1 tiles' loads in flight
     // while one is computed.  The loads are unconditional (rows clamped into
-    // the piece), so the compiler waits for exactly the oldest tile.
-    {
+    // the window), so the compiler waits for exactly the oldest tile.  A
+    // paged cache walks the piece in row windows whose pages fit the LDS
+    // copy of the block table (one window unless the piece spans more than
+    // kPageWindow pages).
+    for (int w0 = ta; w0 < tb; w0 = tend) {
+        if constexpr (SRC == kSrcPaged) {
+            wpage0 = w0 >> a.page_shift;
+            tend = (int)min((long long)tb, (long long)(wpage0 + kPageWindow) << a.page_shift);
+            const int np = ((tend - 1) >> a.page_shift) - wpage0 + 1;
+            const int32_t* bt = a.block_table + (int64_t)pc.b * a.max_pages + wpage0;
+            wave_lds_fence();            // the previous window's page reads are done
+            for (int i = lane; i < np; i += kWave) sm.pages[i] = bt[i];
+            wave_lds_fence();
+        }
         constexpr int NBUF = mfa_buffers<NB>();
         uint4 kb[NBUF][NK], vb[NBUF][NLV];
-        int t0 = ta;
-        const int ntile = (tb - ta + 15) / 16;
+        int t0 = w0;
+        const int ntile = (tend - w0 + 15) / 16;
 #pragma unroll
         for (int u = 0; u < NBUF - 1; ++u) load_tile(t0 + 16 * u, kb[u], vb[u]);
         for (int it = 0; it < ntile; it += NBUF) {
@@ -1613,7 +1673,7 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NB>
+template <int D, int NB, int SRC>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const Args a, const int R, const int n_rb)
 {
@@ -1639,7 +1699,7 @@ decode_mfa(const Args a, const int R, const int n_rb)
     Piece pc;
     while (it.next(a, sm.lens, 0, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB, SRC>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -1740,14 +1800,25 @@ static DecodeFn pick_mqk(int rb)
     }
 }
 
+template <int SRC>
+static DecodeFn pick_mfa(const Plan& p)
+{
+    switch (p.row_block) {
+    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC> : decode_mfa<128, 1, SRC>;
+    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC> : decode_mfa<128, 2, SRC>;
+    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC> : decode_mfa<128, 4, SRC>;
+    default: return nullptr;
+    }
+}
+
 static DecodeFn pick(const Plan& p)
 {
     if (p.path == Path::MFMA) {
         if (!p.kv_bf16) return nullptr;
-        switch (p.row_block) {
-        case 16: return p.D == 64 ? decode_mfa<64, 1> : decode_mfa<128, 1>;
-        case 32: return p.D == 64 ? decode_mfa<64, 2> : decode_mfa<128, 2>;
-        case 64: return p.D == 64 ? decode_mfa<64, 4> : decode_mfa<128, 4>;
+        switch (p.src) {
+        case kSrcCache: return pick_mfa<kSrcCache>(p);
+        case kSrcAppend: return pick_mfa<kSrcAppend>(p);
+        case kSrcPaged: return pick_mfa<kSrcPaged>(p);
         default: return nullptr;
         }
     }

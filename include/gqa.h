@@ -113,7 +113,8 @@ typedef struct {
 
 /*
  * gqa_decode -- out = grouped-query attention (see top of file).
- * One kernel launch.  Uses a workspace owned by the library: one buffer per
+ * One kernel launch (two when the plan merges split segments in a combine
+ * kernel, gqa_plan_t.combine).  Uses a workspace owned by the library: one buffer per
  * device, grown on demand (hipMalloc and a zero fill, after waiting for the
  * device) and kept until process exit.  Calls that run concurrently on
  * different streams of one device must use gqa_decode_ws with their own
@@ -154,6 +155,60 @@ gqa_status_t gqa_decode_ex(const gqa_shape_t *shape, const void *q,
                            const int32_t *seq_lens, float scale, void *out,
                            void *workspace, size_t ws_bytes,
                            const gqa_options_t *opts, void *stream);
+
+/*
+ * gqa_decode_append -- the decode step with its new tokens' K/V appended:
+ * the sq new rows of every (sequence b, KV head g), k_new / v_new
+ * [B, G, sq, D] (dtype of the caches), are stored into the caches at rows
+ * L_b - sq .. L_b - 1 (L_b = clamped seq_lens[b], which counts them; rows
+ * that would fall below 0 are dropped), and attention runs over rows
+ * 0 .. L_b - 1 as in gqa_decode -- one pass: the new rows are read from
+ * k_new / v_new, so the result does not depend on the order of the stores.
+ * The rest of the caches is not modified.  This is the incremental decode
+ * loop's append-then-attend step ("GQA (Grouped-Query Attention) 분석",
+ * section "동작 원리", items 2 "Projection과 RoPE" and 3 "Incremental
+ * decode").
+ * bf16 only (GQA_PATH_MFMA; another path is GQA_ERR_UNSUPPORTED).
+ * workspace NULL with ws_bytes 0: the library-owned workspace.
+ */
+gqa_status_t gqa_decode_append(const gqa_shape_t *shape, const void *q,
+                               const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache,
+                               const int32_t *seq_lens, float scale, void *out,
+                               void *workspace, size_t ws_bytes,
+                               const gqa_options_t *opts, void *stream);
+
+/* Shape of a paged cache: page pools k_pages / v_pages [num_pages, G,
+ * page_size, D]; block_table [B, max_pages] int32 (device) lists each
+ * sequence's pages in order, so row t of sequence b is row
+ * t % page_size of page block_table[b][t / page_size].  The capacity per
+ * sequence is T = page_size * max_pages.  page_size: a power of two in
+ * [16, 65536]. */
+typedef struct {
+    int32_t B, H, G, sq, D;
+    int32_t page_size, num_pages, max_pages;
+    int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
+} gqa_paged_shape_t;
+
+/* Device scratch bytes gqa_decode_paged needs (0 on bad shape). */
+size_t gqa_paged_workspace_bytes(const gqa_paged_shape_t *shape);
+
+/*
+ * gqa_decode_paged -- gqa_decode over a paged cache (see gqa_paged_shape_t):
+ * the same result as gqa_decode on the cache the block table describes
+ * (paging changes only where cache rows live, so it composes with GQA:
+ * "GQA (Grouped-Query Attention) 분석", section "장단점" and the checklist
+ * of item 4 of "동작 원리").  Only the table entries for rows below L_b are
+ * read; an entry outside [0, num_pages) is clamped into it (no fault, but
+ * the result is then meaningless).  bf16 only (GQA_PATH_MFMA).
+ * workspace NULL with ws_bytes 0: the library-owned workspace.
+ */
+gqa_status_t gqa_decode_paged(const gqa_paged_shape_t *shape, const void *q,
+                              const void *k_pages, const void *v_pages,
+                              const int32_t *block_table,
+                              const int32_t *seq_lens, float scale, void *out,
+                              void *workspace, size_t ws_bytes,
+                              const gqa_options_t *opts, void *stream);
 
 /* Fill *plan for shape and opts (opts may be NULL).  Host only, no GPU work. */
 gqa_status_t gqa_plan(const gqa_shape_t *shape, const gqa_options_t *opts,

@@ -166,3 +166,68 @@ def decode_row_f64(q_row, k_b, v_b, H: int, sq: int, h: int, s: int,
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Cache variants.  Both are the plain definition applied to the cache they
+# describe: the rows are put where the variant says, with numpy indexing, and
+# the float64 oracle above runs on the result.
+# ---------------------------------------------------------------------------
+def append_rows(k_new, v_new, k_cache, v_cache, seq_lens=None):
+    """The caches after storing the sq new tokens of every (b, g): token s goes
+    to row L_b - sq + s (L_b = min(seq_lens[b], T), which counts the new
+    tokens); a token whose row would be negative is dropped.  Appending to the
+    cache before attending is the incremental decode loop of "GQA
+    (Grouped-Query Attention) 분석", section "동작 원리", items 2 and 3.
+    Returns new float64 arrays; the inputs are not modified."""
+    kn, vn = _f64(k_new), _f64(v_new)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    B, G, T, D = kc.shape
+    sq = kn.shape[2]
+    if kn.shape != (B, G, sq, D) or vn.shape != kn.shape or vc.shape != kc.shape:
+        raise ValueError("expected k_new/v_new [B,G,sq,D] and caches [B,G,T,D]")
+    lens = [T] * B if seq_lens is None else [min(max(int(x), 0), T) for x in _i32(seq_lens)]
+    for b in range(B):
+        for s in range(sq):
+            row = lens[b] - sq + s
+            if row >= 0:
+                kc[b, :, row, :] = kn[b, :, s, :]
+                vc[b, :, row, :] = vn[b, :, s, :]
+    return kc, vc
+
+
+def decode_append_f64(q, k_new, v_new, k_cache, v_cache, seq_lens=None, scale=None,
+                      threads: int = 1):
+    """Append (see append_rows), then decode.  Returns (out, k_after, v_after)."""
+    kc, vc = append_rows(k_new, v_new, k_cache, v_cache, seq_lens)
+    return decode_f64(q, kc, vc, seq_lens, scale, threads=threads), kc, vc
+
+
+def gather_pages(pages, block_table, seq_lens=None):
+    """The contiguous [B, G, T, D] cache a paged one describes: row t of
+    sequence b is row t % page_size of page block_table[b, t // page_size]
+    of pages [num_pages, G, page_size, D]; T = page_size * max_pages.  Only
+    the pages that hold rows below L_b are looked up; the other rows are NaN
+    (the definition never reads them)."""
+    pg = _f64(pages)
+    bt = _i32(block_table).astype(np.int64)
+    num_pages, G, ps, D = pg.shape
+    B, max_pages = bt.shape
+    T = ps * max_pages
+    lens = [T] * B if seq_lens is None else [min(max(int(x), 0), T) for x in _i32(seq_lens)]
+    out = np.full((B, G, T, D), np.nan, dtype=np.float64)
+    for b in range(B):
+        for i in range((lens[b] + ps - 1) // ps):
+            p = int(bt[b, i])
+            if not 0 <= p < num_pages:
+                raise ValueError("block_table[%d, %d] = %d is not a page" % (b, i, p))
+            out[b, :, i * ps:(i + 1) * ps, :] = pg[p]
+    return out
+
+
+def decode_paged_f64(q, k_pages, v_pages, block_table, seq_lens=None, scale=None,
+                     threads: int = 1):
+    """Decode over a paged cache: gather_pages, then the oracle."""
+    k = gather_pages(k_pages, block_table, seq_lens)
+    v = gather_pages(v_pages, block_table, seq_lens)
+    return decode_f64(q, k, v, seq_lens, scale, threads=threads)

@@ -78,6 +78,7 @@ def test_workload_full(gqa, orc, name):
     ("sweep_b16_h32_g8_d128_t16384_sq2", (3, 9)),
     ("sweep_b16_h32_g4_d128_t16384_sq2", (1, 14)),
     ("sweep_b16_h32_g1_d128_t16384_sq2", (0, 7, 15)),
+    ("multitoken_b8_h32_g8_d128_t4096_sq64", (0, 5)),
 ])
 def test_workload_sampled_rows(gqa, orc, name, rows):
     """Full-size workloads: inputs drawn on the GPU (same recipe, device
@@ -114,6 +115,9 @@ EDGE = [
     (2, 32, 1, 128, 300, 2, "bf16", [300, 123]),         # R=64: four 16-row blocks per wave
     (2, 32, 1, 64, 200, 3, "bf16", [200, 50]),           # R=96: two 64-row segments, second half live
     (2, 24, 1, 128, 150, 2, "bf16", [150, 149]),         # R=48: last 16-row block padding only
+    (2, 8, 2, 128, 300, 33, "bf16", [300, 40]),          # R=132: three 64-row segments
+    (1, 32, 8, 64, 200, 64, "bf16", [200]),              # sq=64, R=256
+    (1, 4, 1, 64, 100, 64, "bf16", [10]),                # sq > L: the first 54 new tokens see nothing
 ]
 
 
