@@ -129,6 +129,11 @@ def main(argv=None):
     ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_qk"])
     ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "combine"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "append", "paged"],
+                    help="decode: gqa_decode; append: gqa_decode_append (the sq new tokens' K/V "
+                         "stored and attended in one pass); paged: gqa_decode_paged over a "
+                         "randomly ordered page pool")
+    ap.add_argument("--page-size", type=int, default=16)
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -171,9 +176,34 @@ def main(argv=None):
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     stream = torch.cuda.current_stream(dev)
 
-    def call():
-        gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
-                   workgroups=args.workgroups, merge=merge, stream=stream)
+    if args.mode == "append":
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 7)
+        kn = torch.randn(w.B, w.G, w.sq, w.D, generator=gen, device=dev).to(x["k"].dtype)
+        vn = torch.randn(w.B, w.G, w.sq, w.D, generator=gen, device=dev).to(x["k"].dtype)
+        ub += 2 * w.B * w.G * w.sq * w.D * kv_elem_bytes(w.dtype)      # the stored rows
+
+        def call():
+            gqa.decode_append(x["q"], kn, vn, x["k"], x["v"], x["seq_lens"], None, out, path=path,
+                              workgroups=args.workgroups, merge=merge, stream=stream)
+    elif args.mode == "paged":
+        ps = args.page_size
+        n = w.T // ps
+        perm = torch.randperm(w.B * n, generator=torch.Generator().manual_seed(w.seed + 11))
+        kp = torch.empty(w.B * n, w.G, ps, w.D, dtype=x["k"].dtype, device=dev)
+        vp = torch.empty_like(kp)
+        idx = perm.view(w.B, n).to(dev)
+        kp[idx.reshape(-1)] = x["k"].view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
+        vp[idx.reshape(-1)] = x["v"].view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
+        bt = idx.to(torch.int32).contiguous()
+        ub += int(sum((int(L) + ps - 1) // ps for L in x["seq_lens"].clamp(0, w.T).tolist())) * 4
+
+        def call():
+            gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], None, out, path=path,
+                             workgroups=args.workgroups, merge=merge, stream=stream)
+    else:
+        def call():
+            gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
+                       workgroups=args.workgroups, merge=merge, stream=stream)
 
     for _ in range(args.warmup):
         if not args.no_flush:
@@ -239,8 +269,13 @@ def main(argv=None):
         import oracle
         b = 0
         xb = {k: v[b:b + 1].cpu() for k, v in x.items()}
-        want = oracle.decode_f64(xb["q"], xb["k"], xb["v"], xb["seq_lens"],
-                                 1.0 / math.sqrt(w.D), threads=8)
+        if args.mode == "append":
+            # the cache already holds the appended rows (every step stores the same ones)
+            want, _, _ = oracle.decode_append_f64(xb["q"], kn[b:b + 1].cpu(), vn[b:b + 1].cpu(), xb["k"],
+                                                  xb["v"], xb["seq_lens"], 1.0 / math.sqrt(w.D), threads=8)
+        else:
+            want = oracle.decode_f64(xb["q"], xb["k"], xb["v"], xb["seq_lens"],
+                                     1.0 / math.sqrt(w.D), threads=8)
         parity = float(np.abs(out[b:b + 1].double().cpu().numpy() - want).max())
     except Exception as e:  # noqa: BLE001
         log("[bench] parity spot check skipped: %s" % e)
@@ -248,7 +283,7 @@ def main(argv=None):
     gbs = ub / (ms * 1e-3) / 1e9
     achieved = gbs      # one kernel per step: the step is the kernel
     sha = kernel_source_sha()
-    traffic = load_traffic(w.name, sha)
+    traffic = load_traffic(w.name if args.mode == "decode" else "%s_%s" % (w.name, args.mode), sha)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -271,6 +306,7 @@ def main(argv=None):
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
             "combine_kernel": bool(plan["combine"]),
+            "mode": args.mode,
         },
         "us_per_step": round(ms * 1e3, 2),
         "timing": "device time per step: K steps back to back after cache sweeps, minus the sweeps alone",

@@ -1404,20 +1404,37 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     const int la = pc.L - a.sq;
     const int64_t nslab = ((int64_t)pc.b * a.G + pc.g) * a.sq * D;
     int wpage0 = 0;                      // paged: first page of the LDS window
-    auto row_addr = [&](const void* base, const void* fresh, int t) -> const char* {
+    bool wnew = false;                   // append: the window holds the new tokens' rows
+    int tend = tb;                       // end of the current row window
+    // paged: pages of the rows the next load_tile reads (K row, V rows),
+    // looked up one tile ahead so the LDS latency hides behind a compute_tile
+    int pgk = 0, pgv[NLV];
+    auto lookup = [&](int t0) {
         if constexpr (SRC == kSrcPaged) {
-            const int pg = min(max(sm.pages[(t >> a.page_shift) - wpage0], 0), a.num_pages - 1);
+            pgk = sm.pages[(min(t0 + col, tend - 1) >> a.page_shift) - wpage0];
+#pragma unroll
+            for (int j = 0; j < NLV; ++j)
+                pgv[j] = sm.pages[(min(t0 + (lane + kWave * j) / CPR, tend - 1) >> a.page_shift) - wpage0];
+        } else {
+            (void)t0;
+        }
+    };
+    auto row_addr = [&](const void* base, const void* fresh, int pg, int t) -> const char* {
+        if constexpr (SRC == kSrcPaged) {
+            (void)fresh;
+            pg = min(max(pg, 0), a.num_pages - 1);
             const int64_t r = (((int64_t)pg * a.G + pc.g) << a.page_shift) + (t & ((1 << a.page_shift) - 1));
             return static_cast<const char*>(base) + r * D * 2;
         } else if constexpr (SRC == kSrcAppend) {
-            return t >= la ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * 2
-                           : static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
+            (void)pg;
+            return wnew ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * 2
+                        : static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
         } else {
             (void)fresh;
+            (void)pg;
             return static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
         }
     };
-    int tend = tb;                       // end of the current row window
 
     // Rows past the window's end re-read its last row (valid): their weights
     // are exactly 0, so no row at or beyond the end is read and no branch
@@ -1425,14 +1442,15 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     // 8 kg + 32 s ..; V: chunk c = lane + 64 j is row c / CPR, elements
     // 8 (c % CPR) ..
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
-        const char* kr = row_addr(a.k, a.k_new, min(t0 + col, tend - 1)) + 16 * kg;
+        const char* kr = row_addr(a.k, a.k_new, pgk, min(t0 + col, tend - 1)) + 16 * kg;
 #pragma unroll
         for (int s = 0; s < NK; ++s) kk[s] = load16_stream(kr + 64 * s);
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
-            vv[j] = load16_stream(row_addr(a.v, a.v_new, min(t0 + c / CPR, tend - 1)) + (c % CPR) * 16);
+            vv[j] = load16_stream(row_addr(a.v, a.v_new, pgv[j], min(t0 + c / CPR, tend - 1)) + (c % CPR) * 16);
         }
+        lookup(t0 + 16);
     };
 
     auto compute_tile = [&](int t0, const uint4* kk, const uint4* vv) {
@@ -1443,7 +1461,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         }
         if constexpr (SRC == kSrcAppend) {
             // the first row block's pieces store the new tokens' rows into the cache
-            if (pc.rb == 0) {
+            if (wnew && pc.rb == 0) {
                 const int tk = t0 + col;
                 if (tk >= la && tk < tend) {
                     char* kr = static_cast<char*>(const_cast<void*>(a.k)) + (slab + (int64_t)tk * D) * 2 + 16 * kg;
@@ -1519,6 +1537,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     // paged cache walks the piece in row windows whose pages fit the LDS
     // copy of the block table (one window unless the piece spans more than
     // kPageWindow pages).
+    // An append walks the cache rows below L - sq, then the new tokens' rows,
+    // as two windows (so a window reads one source, chosen once).
     for (int w0 = ta; w0 < tb; w0 = tend) {
         if constexpr (SRC == kSrcPaged) {
             wpage0 = w0 >> a.page_shift;
@@ -1528,7 +1548,11 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             wave_lds_fence();            // the previous window's page reads are done
             for (int i = lane; i < np; i += kWave) sm.pages[i] = bt[i];
             wave_lds_fence();
+        } else if constexpr (SRC == kSrcAppend) {
+            wnew = w0 >= la;
+            tend = wnew ? tb : min(tb, la);
         }
+        lookup(w0);
         constexpr int NBUF = mfa_buffers<NB>();
         uint4 kb[NBUF][NK], vb[NBUF][NLV];
         int t0 = w0;

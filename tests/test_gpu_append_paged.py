@@ -3,9 +3,10 @@ the C ABI: gqa_decode_append (new tokens stored into the cache and attended
 in one pass) and gqa_decode_paged (page pool + block table).
 
 Tolerances as for gqa_decode (bf16 inputs, fp32 accumulation: 2e-3 max
-abs).  The cache rows an append writes are compared bit for bit; both
-variants are also compared bit for bit with gqa_decode on the cache they
-describe (same plan, same arithmetic)."""
+abs).  The cache rows an append writes are compared bit for bit; a paged
+decode is also compared bit for bit with gqa_decode on the cache it
+describes (same plan, same arithmetic), an append to within 2e-5 (its
+tiles restart at the first new row)."""
 import math
 
 import numpy as np
@@ -67,10 +68,11 @@ def test_append_matches_oracle_and_decode(gqa, orc, case):
     assert _err(got, want) <= TOL
     assert np.array_equal(kc.double().cpu().numpy(), k_after)
     assert np.array_equal(vc.double().cpu().numpy(), v_after)
-    # the same as gqa_decode on the appended cache, bit for bit
+    # the same as gqa_decode on the appended cache, to rounding (the append
+    # starts a new tile at row L - sq, so the tiles group rows differently)
     again = gqa.decode(q, kc, vc, sl)
     torch.cuda.synchronize()
-    assert torch.equal(got, again)
+    assert (got - again).abs().max().item() <= 2e-5
 
 
 def test_append_splits_and_merge_modes(gqa, orc):
