@@ -26,7 +26,7 @@ import math
 import os
 import threading
 
-__all__ = ["decode", "decode_append", "decode_paged", "plan", "workspace_bytes",
+__all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "plan", "workspace_bytes",
            "paged_workspace_bytes", "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
@@ -36,13 +36,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
-GQA_F32, GQA_BF16 = 0, 1
+GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
 MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",
-                    "gqa_decode_ex", "gqa_decode_append", "gqa_paged_workspace_bytes",
+                    "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_append", "gqa_paged_workspace_bytes",
                     "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
 
@@ -113,6 +113,9 @@ def load_library():
         lib.gqa_decode_ex.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_ex.restype = ctypes.c_int
+        lib.gqa_decode_fp8.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
+                                       ctypes.c_size_t, ctypes.POINTER(Options), vp]
+        lib.gqa_decode_fp8.restype = ctypes.c_int
         lib.gqa_decode_append.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                           ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_append.restype = ctypes.c_int
@@ -144,6 +147,8 @@ def _dtype_code(dt) -> int:
         return GQA_F32
     if dt == torch.bfloat16:
         return GQA_BF16
+    if dt in (torch.uint8, torch.float8_e4m3fn):
+        return GQA_FP8_E4M3
     return 99  # rejected by the library as unsupported
 
 
@@ -346,5 +351,42 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens=None, scale=None, ou
             block_table.data_ptr(), seq_lens.data_ptr() if seq_lens is not None else None,
             ctypes.c_float(scale), out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len),
             ctypes.byref(opts), ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+    return out
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale=None, v_scale=None, seq_lens=None, scale=None, out=None,
+               *, workgroups=0, merge=0, workspace=None, stream=None):
+    """Decode over an fp8 E4M3 cache: k_codes / v_codes [B,G,T,D] uint8 (or
+    torch.float8_e4m3fn), k_scale / v_scale [G] float32 on the GPU or None
+    (1.0); the value of code c in KV head g is e4m3(c) * scale[g]."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape:
+        raise ValueError("expected q [B,H,sq,D] and k_codes/v_codes [B,G,T,D]")
+    if k_codes.element_size() != 1 or v_codes.element_size() != 1:
+        raise ValueError("k_codes / v_codes must hold one byte per element")
+    G = k_codes.shape[1]
+    ts = [("q", q), ("k_codes", k_codes), ("v_codes", v_codes)]
+    for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc is not None:
+            if sc.dtype != torch.float32 or sc.shape != (G,):
+                raise ValueError("%s must be a float32 [G] tensor" % name)
+            ts.append((name, sc))
+    out = _common_checks(q, ts, seq_lens, out)
+    dev = q.device
+    scale = 1.0 / math.sqrt(q.shape[3]) if scale is None else scale
+    shape = shape_of(q, k_codes, out.dtype)
+    stream = torch.cuda.current_stream(dev) if stream is None else stream
+    ws_ptr, ws_len = _ws(workspace, dev)
+    opts = _options(PATH_AUTO, workgroups, merge)
+    with torch.cuda.device(dev):
+        st = lib.gqa_decode_fp8(
+            ctypes.byref(shape), q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+            k_scale.data_ptr() if k_scale is not None else None,
+            v_scale.data_ptr() if v_scale is not None else None,
+            seq_lens.data_ptr() if seq_lens is not None else None, ctypes.c_float(scale),
+            out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len), ctypes.byref(opts),
+            ctypes.c_void_p(stream.cuda_stream))
     _check(st)
     return out

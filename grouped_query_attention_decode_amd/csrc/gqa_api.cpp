@@ -69,10 +69,12 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         return fail(GQA_ERR_INVALID_ARG, "H (%d) must be a multiple of G (%d)", s->H, s->G);
     if (s->D != 64 && s->D != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", s->D);
     const bool f32 = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32 && s->out_dtype == GQA_F32;
-    const bool bf16 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_BF16 && s->out_dtype == GQA_F32;
+    const bool fp8 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_FP8_E4M3 && s->out_dtype == GQA_F32;
+    const bool bf16 = (s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_BF16 && s->out_dtype == GQA_F32) || fp8;
     if (!f32 && !bf16)
-        return fail(GQA_ERR_UNSUPPORTED, "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32) or (BF16,BF16,F32)",
-                    s->q_dtype, s->kv_dtype, s->out_dtype);
+        return fail(GQA_ERR_UNSUPPORTED,
+                    "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32), (BF16,BF16,F32) or "
+                    "(BF16,FP8_E4M3,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
     if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
         return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
     if ((int64_t)s->B * s->H * s->sq * s->D >= (int64_t)1 << 40)
@@ -94,6 +96,8 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     }
     if ((path_req == GQA_PATH_MFMA || path_req == GQA_PATH_MFMA_QK) && !bf16)
         return fail(GQA_ERR_UNSUPPORTED, "the matrix-core paths need bf16 q/k/v");
+    if (fp8 && (path_req == GQA_PATH_VALU || path_req == GQA_PATH_MFMA_QK))
+        return fail(GQA_ERR_UNSUPPORTED, "an fp8 cache runs on GQA_PATH_MFMA only");
 
     const int R = (int)R64;
     // bf16 goes to the matrix cores (both products unless asked otherwise);
@@ -105,7 +109,8 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->path = gqa::Path::MFMA_QK;
     else
         p->path = gqa::Path::MFMA;
-    p->kv_bf16 = bf16 ? 1 : 0;
+    p->kv_bf16 = bf16 && !fp8 ? 1 : 0;
+    p->kv_fp8 = fp8 ? 1 : 0;
     p->src = 0;
     p->D = s->D;
     p->R = R;
@@ -219,6 +224,8 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // Where the K/V rows come from, beyond the plain [B, G, T, D] caches.
 struct Source {
     int src = 0;                       // gqa kernel source kind (0 cache, 1 append, 2 paged)
+    const float* k_scale = nullptr;    // fp8 cache: per-KV-head scales [G]
+    const float* v_scale = nullptr;
     const void* k_new = nullptr;       // append: [B, G, sq, D]
     const void* v_new = nullptr;
     const int32_t* block_table = nullptr;  // paged: [B, max_pages]
@@ -232,8 +239,10 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan);
     if (st != GQA_OK) return st;
-    if (srcx.src != 0 && plan.path != gqa::Path::MFMA)
+    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
         return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 matrix-core path");
+    if ((srcx.k_scale || srcx.v_scale) && !plan.kv_fp8)
+        return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an fp8 cache only");
     plan.src = srcx.src;
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale must be finite");
     if (shape->B == 0) return ok();
@@ -275,6 +284,8 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.page_shift = srcx.page_shift;
     a.num_pages = srcx.num_pages;
     a.max_pages = srcx.max_pages;
+    a.k_scale = srcx.k_scale;
+    a.v_scale = srcx.v_scale;
 
     hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -324,6 +335,19 @@ gqa_status_t gqa_decode_append(const gqa_shape_t* shape, const void* q, const vo
     sx.src = 1;
     sx.k_new = k_new;
     sx.v_new = v_new;
+    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
+}
+
+gqa_status_t gqa_decode_fp8(const gqa_shape_t* shape, const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                            void* out, void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
+{
+    if (shape && shape->kv_dtype != GQA_FP8_E4M3)
+        return fail(GQA_ERR_INVALID_ARG, "gqa_decode_fp8 needs kv_dtype GQA_FP8_E4M3");
+    Source sx;
+    sx.k_scale = k_scale;
+    sx.v_scale = v_scale;
     const bool lib_ws = workspace == nullptr && ws_bytes == 0;
     return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
 }

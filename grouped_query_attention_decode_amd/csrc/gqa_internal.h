@@ -29,6 +29,7 @@ __host__ __device__ constexpr int slot_floats(int rb, int d) { return rb * d + (
 struct Plan {
     Path path;
     int kv_bf16;        // 1: bf16 q/k/v, 0: fp32
+    int kv_fp8;         // 1: bf16 q, fp8 E4M3 k/v codes with per-KV-head scales
     int D;
     int R;              // (H/G)*sq query rows per KV head
     int row_block;      // rows per segment (power of two <= 16; 16 on the MFMA path)
@@ -62,6 +63,9 @@ struct Args {
     int page_shift;
     int num_pages;
     int max_pages;
+    // fp8 cache: per-KV-head scales [G] (NULL: 1)
+    const float* k_scale;
+    const float* v_scale;
 };
 
 // Queue the decode kernel on stream.

@@ -1204,8 +1204,36 @@ constexpr float kSlack = 8.0f;
 
 // K/V tiles held in registers per wave: 3 (two in flight) measured best; with
 // four 16-row query blocks the accumulators need the room, so 2.
-template <int NB>
-constexpr int mfa_buffers() { return NB >= 4 ? 2 : 3; }
+// fp8 tiles are half the bytes, so twice as many are kept in flight.
+template <int NB, bool KV8>
+constexpr int mfa_buffers() { return KV8 ? (NB >= 4 ? 3 : 5) : (NB >= 4 ? 2 : 3); }
+
+// Head-dim element where the 8 elements of score-product step s start for
+// k group kg (the order of the reduction over d is free as long as K and Q
+// use the same one): bf16 rows are read as 16-byte pieces at 8 kg + 32 s;
+// fp8 rows as 16-code pieces at 16 kg + 64 h, each splitting into steps 2h
+// and 2h + 1.
+template <int D, bool KV8>
+__device__ __forceinline__ int kdim0(int kg, int s)
+{
+    return KV8 ? 16 * kg + 64 * (s >> 1) + 8 * (s & 1) : 8 * kg + 32 * s;
+}
+
+// 16 fp8 E4M3 codes (one 16-byte load, code i in byte i) to 16 bf16 values
+// in order: lo holds codes 0..7, hi codes 8..15.  Every E4M3 value is a bf16
+// number, so the conversion (scale 1) is exact.
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4& c, uint4& lo, uint4& hi)
+{
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+        o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    }
+    lo = make_uint4(o[0], o[1], o[2], o[3]);
+    hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
 
 constexpr int kPageWindow = 1024;        // block-table entries a wave keeps in LDS (paged cache)
 
@@ -1351,15 +1379,18 @@ __device__ __forceinline__ void locate(const Args& a, const int* lens, int units
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
-template <int D, int NB, int SRC>
+template <int D, int NB, int SRC, bool KV8>
 __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
     constexpr int SE = MfaShared<D>::SE;
-    constexpr int CPR = D / 8;           // 16-byte chunks per cache row
+    constexpr int ES = KV8 ? 1 : 2;      // bytes per cache element (fp8 codes or bf16)
+    constexpr int EPC = 16 / ES;         // cache elements per 16-byte chunk
+    constexpr int CPR = D / EPC;         // 16-byte chunks per cache row
     constexpr int NLV = 16 * CPR / kWave;   // V loads per lane per tile
+    constexpr int NLK = KV8 ? D / 64 : NK;  // K loads per lane per tile
     constexpr int RB = 16 * NB;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -1381,10 +1412,10 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         last[nb] = live[nb] ? pc.L - a.sq + (r % a.sq) : -1;
         m_run[nb] = -INFINITY;
         l_run[nb] = 0.0f;
-        const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live[nb] ? 16 * nb + col : 0)) * D + 8 * kg) * 2;
+        const char* qp = static_cast<const char*>(a.q) + (qrow0 + (live[nb] ? 16 * nb + col : 0)) * D * 2;
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
-            const uint4 v = load16(qp + 64 * s);
+            const uint4 v = load16(qp + 2 * kdim0<D, KV8>(kg, s));
             qb[nb][s] = live[nb] ? v : make_uint4(0, 0, 0, 0);
         }
     }
@@ -1393,6 +1424,13 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[nb][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // fp8 cache: the value of a code is decode(code) * scale of its KV head;
+    // K's scale joins the score scale, V's multiplies the output
+    float score_scale = a.scale_log2, out_scale = 1.0f;
+    if constexpr (KV8) {
+        if (a.k_scale) score_scale *= a.k_scale[pc.g];
+        if (a.v_scale) out_scale = a.v_scale[pc.g];
+    }
 
     // Where cache row t of (b, g) lives (byte address of its element 0):
     //   kSrcCache  : the [B, G, T, D] cache;
@@ -1424,15 +1462,15 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             (void)fresh;
             pg = min(max(pg, 0), a.num_pages - 1);
             const int64_t r = (((int64_t)pg * a.G + pc.g) << a.page_shift) + (t & ((1 << a.page_shift) - 1));
-            return static_cast<const char*>(base) + r * D * 2;
+            return static_cast<const char*>(base) + r * D * ES;
         } else if constexpr (SRC == kSrcAppend) {
             (void)pg;
-            return wnew ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * 2
-                        : static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
+            return wnew ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * ES
+                        : static_cast<const char*>(base) + (slab + (int64_t)t * D) * ES;
         } else {
             (void)fresh;
             (void)pg;
-            return static_cast<const char*>(base) + (slab + (int64_t)t * D) * 2;
+            return static_cast<const char*>(base) + (slab + (int64_t)t * D) * ES;
         }
     };
 
@@ -1442,9 +1480,12 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     // 8 kg + 32 s ..; V: chunk c = lane + 64 j is row c / CPR, elements
     // 8 (c % CPR) ..
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
-        const char* kr = row_addr(a.k, a.k_new, pgk, min(t0 + col, tend - 1)) + 16 * kg;
+        const char* kr = row_addr(a.k, a.k_new, pgk, min(t0 + col, tend - 1));
+        // bf16: elements kdim0(kg, s) .. + 7 for step s; fp8: 16 codes from
+        // element 16 kg + 64 h (steps 2h and 2h + 1)
 #pragma unroll
-        for (int s = 0; s < NK; ++s) kk[s] = load16_stream(kr + 64 * s);
+        for (int s = 0; s < NLK; ++s)
+            kk[s] = load16_stream(kr + (KV8 ? 16 * kg + 64 * s : 2 * kdim0<D, KV8>(kg, s)));
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
@@ -1453,11 +1494,29 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         lookup(t0 + 16);
     };
 
-    auto compute_tile = [&](int t0, const uint4* kk, const uint4* vv) {
+    auto compute_tile = [&](int t0, const uint4* kin, const uint4* vv) {
+        uint4 kk[NK];
+        if constexpr (KV8) {
+            // 16 fp8 codes -> two 8-element bf16 operands (exact)
 #pragma unroll
-        for (int j = 0; j < NLV; ++j) {
-            const int c = lane + kWave * j;
-            *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+            for (int h = 0; h < NLK; ++h) fp8x16_to_bf16(kin[h], kk[2 * h], kk[2 * h + 1]);
+#pragma unroll
+            for (int j = 0; j < NLV; ++j) {
+                const int c = lane + kWave * j;
+                uint4 lo, hi;
+                fp8x16_to_bf16(vv[j], lo, hi);
+                uint16_t* dst = &sm.vt[(c / CPR) * SE + (c % CPR) * 16];
+                *reinterpret_cast<uint4*>(dst) = lo;
+                *reinterpret_cast<uint4*>(dst + 8) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NK; ++s) kk[s] = kin[s];
+#pragma unroll
+            for (int j = 0; j < NLV; ++j) {
+                const int c = lane + kWave * j;
+                *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+            }
         }
         if constexpr (SRC == kSrcAppend) {
             // the first row block's pieces store the new tokens' rows into the cache
@@ -1491,7 +1550,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int t = t0 + 4 * kg + jj;
-                sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * a.scale_log2 : -INFINITY;
+                sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * score_scale : -INFINITY;
                 mx = fmaxf(mx, sc[jj]);
             }
             mx = max_x32(max_x16(mx));
@@ -1553,8 +1612,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             tend = wnew ? tb : min(tb, la);
         }
         lookup(w0);
-        constexpr int NBUF = mfa_buffers<NB>();
-        uint4 kb[NBUF][NK], vb[NBUF][NLV];
+        constexpr int NBUF = mfa_buffers<NB, KV8>();
+        uint4 kb[NBUF][NLK], vb[NBUF][NLV];
         int t0 = w0;
         const int ntile = (tend - w0 + 15) / 16;
 #pragma unroll
@@ -1576,7 +1635,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float l = sum_x32(sum_x16(l_run[nb]));
-        inv[nb] = l > 0.0f ? 1.0f / l : 0.0f;
+        inv[nb] = l > 0.0f ? out_scale / l : 0.0f;
         lse[nb] = l > 0.0f ? m_run[nb] + __log2f(l) : -INFINITY;
     }
     const int c_first = cm.of(pc.off);
@@ -1697,7 +1756,7 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NB, int SRC>
+template <int D, int NB, int SRC, bool KV8>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const Args a, const int R, const int n_rb)
 {
@@ -1723,7 +1782,7 @@ decode_mfa(const Args a, const int R, const int n_rb)
     Piece pc;
     while (it.next(a, sm.lens, 0, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB, SRC>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB, SRC, KV8>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -1824,13 +1883,13 @@ static DecodeFn pick_mqk(int rb)
     }
 }
 
-template <int SRC>
+template <int SRC, bool KV8>
 static DecodeFn pick_mfa(const Plan& p)
 {
     switch (p.row_block) {
-    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC> : decode_mfa<128, 1, SRC>;
-    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC> : decode_mfa<128, 2, SRC>;
-    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC> : decode_mfa<128, 4, SRC>;
+    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC, KV8> : decode_mfa<128, 1, SRC, KV8>;
+    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC, KV8> : decode_mfa<128, 2, SRC, KV8>;
+    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC, KV8> : decode_mfa<128, 4, SRC, KV8>;
     default: return nullptr;
     }
 }
@@ -1838,11 +1897,12 @@ static DecodeFn pick_mfa(const Plan& p)
 static DecodeFn pick(const Plan& p)
 {
     if (p.path == Path::MFMA) {
+        if (p.kv_fp8) return p.src == kSrcCache ? pick_mfa<kSrcCache, true>(p) : nullptr;
         if (!p.kv_bf16) return nullptr;
         switch (p.src) {
-        case kSrcCache: return pick_mfa<kSrcCache>(p);
-        case kSrcAppend: return pick_mfa<kSrcAppend>(p);
-        case kSrcPaged: return pick_mfa<kSrcPaged>(p);
+        case kSrcCache: return pick_mfa<kSrcCache, false>(p);
+        case kSrcAppend: return pick_mfa<kSrcAppend, false>(p);
+        case kSrcPaged: return pick_mfa<kSrcPaged, false>(p);
         default: return nullptr;
         }
     }

@@ -61,7 +61,10 @@ typedef enum {
     GQA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed        */
 } gqa_status_t;
 
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype_t;
+/* GQA_FP8_E4M3: OCP FP8 E4M3 ("E4M3FN") codes -- sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormals, no infinities; codes S.1111.111 are
+ * NaN and must not appear in the rows read.  A cache only. */
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2 } gqa_dtype_t;
 
 /* Problem shape.  H: query heads, G: KV heads ("num_key_value_heads"),
  * sq: new query tokens per sequence, T: cache capacity in rows, D: head dim. */
@@ -177,6 +180,25 @@ gqa_status_t gqa_decode_append(const gqa_shape_t *shape, const void *q,
                                const int32_t *seq_lens, float scale, void *out,
                                void *workspace, size_t ws_bytes,
                                const gqa_options_t *opts, void *stream);
+
+/*
+ * gqa_decode_fp8 -- gqa_decode over an fp8 cache: shape->kv_dtype ==
+ * GQA_FP8_E4M3 (q bf16, out fp32), k_cache / v_cache [B, G, T, D] one byte
+ * per element, k_scale / v_scale [G] fp32 on the device (NULL: 1.0): the
+ * cache value of a code c in KV head g is e4m3(c) * scale[g].  KV-cache
+ * quantization changes only the element precision and composes with GQA
+ * ("GQA (Grouped-Query Attention) 분석", section "장단점"); the format and
+ * the per-KV-head scale are this library's choice.  Codes are converted to
+ * bf16 exactly; accumulation is fp32.  GQA_PATH_MFMA only.  gqa_decode and
+ * gqa_decode_ex also take an fp8 shape, with unit scales.
+ * workspace NULL with ws_bytes 0: the library-owned workspace.
+ */
+gqa_status_t gqa_decode_fp8(const gqa_shape_t *shape, const void *q,
+                            const void *k_cache, const void *v_cache,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *seq_lens, float scale, void *out,
+                            void *workspace, size_t ws_bytes,
+                            const gqa_options_t *opts, void *stream);
 
 /* Shape of a paged cache: page pools k_pages / v_pages [num_pages, G,
  * page_size, D]; block_table [B, max_pages] int32 (device) lists each

@@ -231,3 +231,44 @@ def decode_paged_f64(q, k_pages, v_pages, block_table, seq_lens=None, scale=None
     k = gather_pages(k_pages, block_table, seq_lens)
     v = gather_pages(v_pages, block_table, seq_lens)
     return decode_f64(q, k, v, seq_lens, scale, threads=threads)
+
+
+# ---------------------------------------------------------------------------
+# Quantized cache: fp8 E4M3 codes with one scale per KV head.  The pages
+# name KV quantization only as a change of element precision that composes
+# with GQA ("GQA (Grouped-Query Attention) 분석", section "장단점"); the
+# format read here is the OCP FP8 E4M3 ("E4M3FN") code -- sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+# S.1111.111 = NaN -- and the cache value is decode(code) * scale[g].
+# ---------------------------------------------------------------------------
+def fp8_e4m3_value(code: int) -> float:
+    """The real number an E4M3 code stands for (NaN for S.1111.111)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - 7)          # subnormal: 0.m * 2^-6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_FP8_TABLE = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def dequant_fp8(codes, scale) -> np.ndarray:
+    """codes [B, G, T, D] (uint8), scale [G] -> float64 cache values."""
+    c = np.asarray(codes.cpu().numpy() if hasattr(codes, "cpu") else codes).astype(np.int64)
+    sc = _f64(scale)
+    if c.ndim != 4 or sc.shape != (c.shape[1],):
+        raise ValueError("expected codes [B,G,T,D] and scale [G]")
+    return _FP8_TABLE[c] * sc[None, :, None, None]
+
+
+def decode_fp8_f64(q, k_codes, v_codes, k_scale, v_scale, seq_lens=None, scale=None,
+                   threads: int = 1):
+    """Decode over an fp8 cache: dequantize every code (dequant_fp8), then
+    the float64 oracle."""
+    return decode_f64(q, dequant_fp8(k_codes, k_scale), dequant_fp8(v_codes, v_scale), seq_lens,
+                      scale, threads=threads)

@@ -7,6 +7,8 @@ append; its section "장단점" for paging as a layout orthogonal to GQA).
 The pins below fix them against literal small examples and against other
 formulations: the token-by-token incremental decode loop, page-permutation
 invariance and shared pages."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -108,3 +110,60 @@ def test_shared_pages_and_unused_table_entries(oracle_mod):
     assert np.array_equal(got, want)
     with pytest.raises(ValueError):
         oracle_mod.decode_paged_f64(q, kp, vp, bt, [20, 40])     # needs entry -1
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3 cache
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x80, -0.0), (0x38, 1.0), (0xB8, -1.0), (0x3C, 1.5), (0x40, 2.0),
+    (0x7E, 448.0), (0xFE, -448.0),                 # largest finite
+    (0x08, 2.0 ** -6), (0x07, 7 * 2.0 ** -9),     # smallest normal, largest subnormal
+    (0x01, 2.0 ** -9),                             # smallest subnormal
+    (0x28, 0.25), (0x30, 0.5), (0x22, 0.15625),     # 2^-2; 2^-1; (1 + 2/8) * 2^-3
+])
+def test_fp8_e4m3_literal_codes(oracle_mod, code, value):
+    got = oracle_mod.fp8_e4m3_value(code)
+    assert got == value and np.signbit(got) == np.signbit(value)
+
+
+def test_fp8_e4m3_nan_codes_and_library_agreement(oracle_mod):
+    assert np.isnan(oracle_mod.fp8_e4m3_value(0x7F)) and np.isnan(oracle_mod.fp8_e4m3_value(0xFF))
+    # every code, against torch's float8_e4m3fn (a library with the same definition)
+    codes = torch.arange(256, dtype=torch.uint8)
+    lib = codes.view(torch.float8_e4m3fn).double().numpy()
+    ours = np.array([oracle_mod.fp8_e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(lib[ok], ours[ok])
+    # monotone over the positive codes, symmetric in the sign bit
+    pos = ours[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(ours[0x80:0xFF], -ours[:0x7F])
+
+
+def test_fp8_decode_equals_decode_of_dequantized_cache(oracle_mod):
+    """With power-of-two scales every dequantized value is exactly a bf16
+    number, so the fp8 decode equals the bf16 decode of that cache."""
+    B, H, G, D, T, sq = 2, 8, 2, 32, 50, 1
+    gen = torch.Generator().manual_seed(70)
+    kc = torch.randint(0, 256, (B, G, T, D), generator=gen, dtype=torch.uint8)
+    vc = torch.randint(0, 256, (B, G, T, D), generator=gen, dtype=torch.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x38      # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x38
+    ks = torch.tensor([0.25, 2.0 ** -10])
+    vs = torch.tensor([1.0, 0.5])
+    q = torch.randn(B, H, sq, D, generator=gen).to(torch.bfloat16)
+    lens = [50, 9]
+    kd = kc.view(torch.float8_e4m3fn).to(torch.float32) * ks.view(1, G, 1, 1)
+    vd = vc.view(torch.float8_e4m3fn).to(torch.float32) * vs.view(1, G, 1, 1)
+    assert torch.equal(kd.to(torch.bfloat16).to(torch.float32), kd)      # exact in bf16
+    want = oracle_mod.decode_f64(q, kd.to(torch.bfloat16), vd.to(torch.bfloat16), lens)
+    got = oracle_mod.decode_fp8_f64(q, kc, vc, ks, vs, lens)
+    assert np.array_equal(got, want)
+    # scaling V's scale scales the output; K's scale acts as a score scale
+    got2 = oracle_mod.decode_fp8_f64(q, kc, vc, ks, 2 * vs, lens)
+    assert np.array_equal(got2, 2 * got)
+    got3 = oracle_mod.decode_fp8_f64(q, kc, vc, 2 * ks, vs, lens, scale=0.5 / math.sqrt(D))
+    assert np.allclose(got3, oracle_mod.decode_fp8_f64(q, kc, vc, ks, vs, lens, scale=1 / math.sqrt(D)),
+                       rtol=0, atol=1e-12)
