@@ -129,10 +129,11 @@ def main(argv=None):
     ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_qk"])
     ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "combine"])
-    ap.add_argument("--mode", default="decode", choices=["decode", "append", "paged"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "append", "paged", "fp8"],
                     help="decode: gqa_decode; append: gqa_decode_append (the sq new tokens' K/V "
                          "stored and attended in one pass); paged: gqa_decode_paged over a "
-                         "randomly ordered page pool")
+                         "randomly ordered page pool; fp8: gqa_decode_fp8 over E4M3 codes with "
+                         "per-KV-head scales (amax / 448)")
     ap.add_argument("--page-size", type=int, default=16)
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
@@ -200,6 +201,20 @@ def main(argv=None):
         def call():
             gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], None, out, path=path,
                              workgroups=args.workgroups, merge=merge, stream=stream)
+    elif args.mode == "fp8":
+        def quant(t):
+            amax = t.float().abs().amax(dim=(0, 2, 3)).clamp_min(1e-6)
+            sc = (amax / 448.0).float().contiguous()
+            return (t.float() / sc.view(1, -1, 1, 1)).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc
+        kq, ks = quant(x["k"])
+        vq, vs = quant(x["v"])
+        plan = gqa.plan(gqa.shape_of(x["q"], kq), path=path, workgroups=args.workgroups, merge=merge)
+        log("[bench] fp8 plan %s" % plan)
+        ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype) - sum_len * w.G * w.D * 2 + 2 * w.G * 4
+
+        def call():
+            gqa.decode_fp8(x["q"], kq, vq, ks, vs, x["seq_lens"], None, out,
+                           workgroups=args.workgroups, merge=merge, stream=stream)
     else:
         def call():
             gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
@@ -269,7 +284,10 @@ def main(argv=None):
         import oracle
         b = 0
         xb = {k: v[b:b + 1].cpu() for k, v in x.items()}
-        if args.mode == "append":
+        if args.mode == "fp8":
+            want = oracle.decode_fp8_f64(xb["q"], kq[b:b + 1].cpu(), vq[b:b + 1].cpu(), ks.cpu(), vs.cpu(),
+                                         xb["seq_lens"], 1.0 / math.sqrt(w.D), threads=8)
+        elif args.mode == "append":
             # the cache already holds the appended rows (every step stores the same ones)
             want, _, _ = oracle.decode_append_f64(xb["q"], kn[b:b + 1].cpu(), vn[b:b + 1].cpu(), xb["k"],
                                                   xb["v"], xb["seq_lens"], 1.0 / math.sqrt(w.D), threads=8)

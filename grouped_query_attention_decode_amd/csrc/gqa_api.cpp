@@ -133,8 +133,9 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // fit) -- enough loads in flight to saturate HBM; more waves only add
     // pieces, and so partials and merges.
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
-    // then one wave on each of the four SIMDs of a compute unit.
-    const int want = (p->path == gqa::Path::MFMA && p->row_block >= 64) ? 4 : gqa::kWavesPerCU;
+    // then one wave on each of the four SIMDs of a compute unit.  So does an
+    // fp8 cache (half the bytes per tile for the same arithmetic).
+    const int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;
     int occ = gqa::resident_groups_per_cu(*p);
     if (occ <= 0 || occ > want) occ = want;
     int64_t P = (int64_t)device_compute_units() * occ;

@@ -1538,6 +1538,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             }
         }
         s16x4_t ph[NB], pl[NB];
+        // no row of the tile is past the window or after the first new token
+        const bool full = t0 + 16 <= tend && t0 + 15 <= pc.L - a.sq;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1547,11 +1549,22 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
                                                              __builtin_bit_cast(bf16x8_t, qb[nb][s]), s4, 0, 0, 0);
             float sc[4];
             float mx = -INFINITY;
+            if (full) {
+                // every row of the tile is visible to every new token (rows of
+                // padding query rows are not masked either: their results are
+                // never stored)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int t = t0 + 4 * kg + jj;
-                sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * score_scale : -INFINITY;
-                mx = fmaxf(mx, sc[jj]);
+                for (int jj = 0; jj < 4; ++jj) {
+                    sc[jj] = s4[jj] * score_scale;
+                    mx = fmaxf(mx, sc[jj]);
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int t = t0 + 4 * kg + jj;
+                    sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * score_scale : -INFINITY;
+                    mx = fmaxf(mx, sc[jj]);
+                }
             }
             mx = max_x32(max_x16(mx));
             // the four lanes of a query row take the same decision
@@ -1566,7 +1579,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             float pv[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                pv[jj] = (sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run[nb]);
+                // in a full tile every score is finite and so is m_run
+                pv[jj] = (!full && sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run[nb]);
                 l_run[nb] += pv[jj];
             }
             // p = hi + lo, both bf16
