@@ -59,7 +59,7 @@ int device_compute_units()
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Validate the shape and options and build the launch plan.
-gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* p)
+gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* p, int src = 0)
 {
     if (!s) return fail(GQA_ERR_INVALID_ARG, "shape is NULL");
     if (s->B < 0 || s->H <= 0 || s->G <= 0 || s->sq <= 0 || s->T <= 0 || s->D <= 0)
@@ -111,7 +111,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->path = gqa::Path::MFMA;
     p->kv_bf16 = bf16 && !fp8 ? 1 : 0;
     p->kv_fp8 = fp8 ? 1 : 0;
-    p->src = 0;
+    p->src = src;
     p->D = s->D;
     p->R = R;
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
@@ -135,7 +135,13 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
     // then one wave on each of the four SIMDs of a compute unit.  So does an
     // fp8 cache (half the bytes per tile for the same arithmetic).
-    const int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;
+    // More than 16 query rows of a plain bf16 cache: workgroups of
+    // row_block / 16 waves sharing each K/V tile through LDS, two waves per
+    // SIMD.
+    p->wg_waves = (p->path == gqa::Path::MFMA && !p->kv_fp8 && src == 0 && p->row_block >= 32)
+                      ? p->row_block / 16 : 1;
+    int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;
+    if (p->wg_waves > 1) want = gqa::kMultiWaveWavesPerCU / p->wg_waves;
     int occ = gqa::resident_groups_per_cu(*p);
     if (occ <= 0 || occ > want) occ = want;
     int64_t P = (int64_t)device_compute_units() * occ;
@@ -238,7 +244,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
                  bool library_ws, const gqa_options_t* opts, void* stream, const Source& srcx = Source())
 {
     gqa::Plan plan;
-    gqa_status_t st = make_plan(shape, opts, &plan);
+    gqa_status_t st = make_plan(shape, opts, &plan, srcx.src);
     if (st != GQA_OK) return st;
     if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
         return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 matrix-core path");
@@ -387,7 +393,7 @@ size_t gqa_paged_workspace_bytes(const gqa_paged_shape_t* shape)
     int sh = 0;
     if (paged_as_shape(shape, &s, &sh) != GQA_OK) return 0;
     gqa::Plan plan;
-    if (make_plan(&s, nullptr, &plan) != GQA_OK) return 0;
+    if (make_plan(&s, nullptr, &plan, 2) != GQA_OK) return 0;
     return plan.ws_bytes;
 }
 

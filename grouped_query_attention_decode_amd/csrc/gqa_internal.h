@@ -14,6 +14,7 @@ constexpr int kMaxRowBlock = 16;   // query rows per VALU segment
 constexpr int kMaxSegments = 1 << 18;  // (sequence, KV head, row block) triples per call
 constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (measured best)
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
+constexpr int kMultiWaveWavesPerCU = 8;   // multi-wave matrix-core kernel: two waves per SIMD
 constexpr int64_t kMergeBytesInKernel = 64 << 10;  // larger merges go to the combine kernel
 // The workspace starts with one arrival counter per possible segment, at a
 // fixed place whatever the shape, so counters never land on another call's
@@ -38,6 +39,7 @@ struct Plan {
     int deferred;       // 1: split segments are merged by a second, parallel kernel
     int slot_rows;      // matrix-core path: rows per partial slot, min(row_block, R)
     int src;            // matrix-core path: 0 cache, 1 cache + appended tokens, 2 paged cache
+    int wg_waves;       // waves per workgroup: 1, or 2 / 4 for the multi-wave matrix-core kernel
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };

@@ -628,7 +628,7 @@ __device__ void zero_empty_sequences(const Args& a, int P, int p)
     for (int b = p; b < a.B; b += P) {
         if (clamp_len(a.seq_lens, b, a.T) != 0) continue;
         float* o = a.out + (int64_t)b * rows * D;
-        for (int idx = threadIdx.x; idx < rows * D; idx += kWave) o[idx] = 0.0f;
+        for (int idx = threadIdx.x; idx < rows * D; idx += blockDim.x) o[idx] = 0.0f;
     }
 }
 
@@ -1803,6 +1803,262 @@ decode_mfa(const Args a, const int R, const int n_rb)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core pass for groups of more than 16 query rows.  A workgroup of NW
+// waves (NW = 2 or 4) owns segments of 16 NW query rows; wave w computes
+// rows 16 w .. 16 w + 15 as decode_mfa computes one block, and the NW waves
+// share every K/V tile: the workgroup loads it once (each thread a share of
+// its 16-byte chunks, two tiles ahead in registers) and stages it in LDS,
+// double-buffered, one barrier per tile.  Compared with one wave carrying
+// all the blocks, the blocks' arithmetic runs on NW SIMDs at once, and a
+// split segment's merge is shared by the NW waves too.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct MfwShared {
+    static constexpr int SK = D + 8;    // K row stride (bf16): the 16 rows of an A-operand read hit distinct banks
+    static constexpr int SE = D + 16;   // V row stride, as in MfaShared
+    alignas(16) uint16_t kt[2][16 * SK];
+    alignas(16) uint16_t vt[2][16 * SE];
+    int lens[kLensWindow];              // clamped seq_lens[i]
+    int merge;                          // 1 when this workgroup arrived last for the current piece
+};
+
+template <int D, int NW>
+__device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, int R, const Piece& pc,
+                                          const ChunkMap& cm, int chunk, int n_rb, Pending* pd)
+{
+    constexpr int NK = D / 32;
+    constexpr int NC = D / 16;
+    constexpr int SK = MfwShared<D, NW>::SK;
+    constexpr int SE = MfwShared<D, NW>::SE;
+    constexpr int CPR = D / 8;           // 16-byte chunks per cache row
+    constexpr int NT = kWave * NW;       // threads of the workgroup
+    constexpr int NCH = (16 * CPR + NT - 1) / NT;   // K chunks (and V chunks) per thread per tile
+    constexpr int RB = 16 * NW;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int col = lane & 15;
+    const int kg = lane >> 4;
+    const int ta = pc.ta, tb = pc.tb;
+    const int row0 = pc.rb * RB;
+    const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
+    const int r = row0 + 16 * w + col;   // this lane's query row (score / output column)
+    const bool live = r < R;
+    const int last = live ? pc.L - a.sq + (r % a.sq) : -1;
+    // with D = 64 and four waves half of the threads have no chunk
+    auto has = [&](int j) { return (16 * CPR) % NT == 0 || tid + NT * j < 16 * CPR; };
+
+    uint4 qb[NK];
+    {
+        const char* qp = static_cast<const char*>(a.q) + (qrow0 + (live ? 16 * w + col : 0)) * D * 2;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            const uint4 v = load16(qp + 2 * kdim0<D, false>(kg, s));
+            qb[s] = live ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4_t acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
+    const char* kbase = static_cast<const char*>(a.k) + slab * 2;
+    const char* vbase = static_cast<const char*>(a.v) + slab * 2;
+
+    // chunk c = tid + NT j of a tile: row c / CPR, elements 8 (c % CPR) ..;
+    // rows past the piece's end re-read its last row (weight 0)
+    auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = min(tid + NT * j, 16 * CPR - 1);
+            const int64_t off = ((int64_t)min(t0 + c / CPR, tb - 1) * D + (c % CPR) * 8) * 2;
+            kk[j] = load16_stream(kbase + off);
+            vv[j] = load16_stream(vbase + off);
+        }
+    };
+    auto stage = [&](int buf, const uint4* kk, const uint4* vv) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = tid + NT * j;
+            if (!has(j)) continue;
+            *reinterpret_cast<uint4*>(&sm.kt[buf][(c / CPR) * SK + (c % CPR) * 8]) = kk[j];
+            *reinterpret_cast<uint4*>(&sm.vt[buf][(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+        }
+    };
+    auto compute = [&](int buf, int t0) {
+        uint4 kk[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            kk[s] = *reinterpret_cast<const uint4*>(&sm.kt[buf][col * SK + kdim0<D, false>(kg, s)]);
+        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                         __builtin_bit_cast(bf16x8_t, qb[s]), s4, 0, 0, 0);
+        const bool full = t0 + 16 <= tb && t0 + 15 <= pc.L - a.sq;
+        float sc[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0 + 4 * kg + jj;
+            sc[jj] = (full || (t < tb && t <= last)) ? s4[jj] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[jj]);
+        }
+        mx = max_x32(max_x16(mx));
+        const bool need = mx > m_run + kSlack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float al = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+            m_run = need ? mx : m_run;
+            l_run *= al;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] *= al;
+        }
+        float pv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            pv[jj] = (!full && sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run);
+            l_run += pv[jj];
+        }
+        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
+        const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
+        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
+        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
+        const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
+        const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+        const uint16_t* vr = sm.vt[buf] + 4 * kg * SE + col;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const s16x4_t va = {(short)vr[16 * c], (short)vr[SE + 16 * c], (short)vr[2 * SE + 16 * c],
+                                (short)vr[3 * SE + 16 * c]};
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[c], 0, 0, 0);
+        }
+    };
+
+    // Tile i is computed from LDS buffer i & 1 while tile i + 1 is staged
+    // into the other buffer and tile i + 2 is in flight; the barrier after
+    // each tile orders both for the next.
+    {
+        uint4 kr[3][NCH], vr[3][NCH];
+        const int ntile = (tb - ta + 15) / 16;
+        load_tile(ta, kr[0], vr[0]);
+        load_tile(ta + 16, kr[1], vr[1]);
+        stage(0, kr[0], vr[0]);
+        __syncthreads();
+        for (int it = 0; it < ntile; it += 3) {
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int i = it + u;
+                if (i >= ntile) break;
+                load_tile(ta + 16 * (i + 2), kr[(u + 2) % 3], vr[(u + 2) % 3]);
+                if (i + 1 < ntile) stage((i + 1) & 1, kr[(u + 1) % 3], vr[(u + 1) % 3]);
+                compute(i & 1, ta + 16 * i);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- end of the piece ------------------------------------------------------
+    const float l = sum_x32(sum_x16(l_run));
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lse = l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+    const int c_first = cm.of(pc.off);
+    const int npieces = cm.of(pc.off + pc.L - 1) - c_first + 1;
+    if (npieces == 1) {
+        if (live) {
+            float* o = a.out + (qrow0 + 16 * w + col) * D + 4 * kg;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[c] * inv;
+        }
+        return false;
+    }
+    const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+    const MSlots ms = mslots<D>(a);
+    const int mine = ms.base(chunk, cm.start(chunk) >= pc.off ? 0 : 1);
+    if (live) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const f32x4_t o = acc[c] * inv;
+            const float ov[4] = {o[0], o[1], o[2], o[3]};
+            store4_coherent(part, mine + (16 * w + col) * D + 16 * c + 4 * kg, ov);
+        }
+        if (kg == 0) store_coherent(part, mine + ms.lse + 16 * w + col, lse);
+    }
+    pd->seg = (pc.b * a.G + pc.g) * n_rb + pc.rb;
+    pd->p_first = c_first;
+    pd->npieces = npieces;
+    pd->off = pc.off;
+    pd->qrow0 = qrow0;
+    pd->row0 = row0;
+    return true;
+}
+
+// Merge of this wave's 16 rows of a segment (rows r0 .. r0 + rows - 1 of
+// its slots), choosing the lane layout by the number of live rows.
+template <int D>
+__device__ __forceinline__ void merge_block16(const Args& a, const Pending& pd, int lane, int r0, int rows,
+                                              const ChunkMap& cm)
+{
+    if (rows > 8)
+        merge_pieces<D, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, cm);
+    else if (rows > 4)
+        merge_pieces<D, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, cm);
+    else if (rows > 2 || D == 64)
+        merge_pieces<D, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, cm);
+    else
+        merge_pieces<D, 1, 16>(a, pd, lane, r0, rows, cm);
+}
+
+template <int D, int NW>
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfw(const Args a, const int R, const int n_rb)
+{
+    __shared__ MfwShared<D, NW> sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    zero_empty_sequences<D>(a, P, p);
+    for (int i = tid; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
+    __syncthreads();
+    const int units = a.G * n_rb;
+    const long long W = total_rows(a, sm.lens) * units;
+    if (W == 0) return;
+    const ChunkMap cm = make_map(W, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer units than workgroups
+    const long long A = cm.start(chunk), E = cm.start(chunk + 1);
+    int fb;
+    long long fe;
+    locate(a, sm.lens, units, A, fb, fe);
+    PieceIter it;
+    it.init_range(A, E, fb, fe, a.G, n_rb);
+    Piece pc;
+    while (it.next(a, sm.lens, 0, pc)) {
+        Pending pd;
+        if (mfw_piece<D, NW>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores complete at device scope
+            __syncthreads();                 // ... and every other wave's
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                sm.merge = old == pd.npieces - 1;
+                if (sm.merge) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (sm.merge) {
+                const int rows = min(16, min(16 * NW, R - pd.row0) - 16 * w);
+                if (rows > 0) merge_block16<D>(a, pd, lane, 16 * w, rows, cm);
+            }
+            __syncthreads();                 // sm.merge is rewritten by the next piece
+        }
+    }
+}
+
 // Combine pass for a deferred plan: one wave per (segment, query row) of a
 // split segment merges the row's partials, in chunk order (the same
 // log2-sum-exp merge as the in-kernel one).  Lane l holds elements
@@ -1910,6 +2166,12 @@ static DecodeFn pick_mfa(const Plan& p)
 
 static DecodeFn pick(const Plan& p)
 {
+    if (p.path == Path::MFMA && p.wg_waves > 1) {
+        if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
+        if (p.wg_waves == 2) return p.D == 64 ? decode_mfw<64, 2> : decode_mfw<128, 2>;
+        if (p.wg_waves == 4) return p.D == 64 ? decode_mfw<64, 4> : decode_mfw<128, 4>;
+        return nullptr;
+    }
     if (p.path == Path::MFMA) {
         if (p.kv_fp8) return p.src == kSrcCache ? pick_mfa<kSrcCache, true>(p) : nullptr;
         if (!p.kv_bf16) return nullptr;
@@ -1934,7 +2196,7 @@ int resident_groups_per_cu(const Plan& p)
     DecodeFn fn = pick(p);
     if (!fn) return 0;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), kWave, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), kWave * p.wg_waves, 0) !=
         hipSuccess) {
         (void)hipGetLastError();
         return 0;
@@ -1973,7 +2235,7 @@ hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
         comb = pick_combine(p);
         if (!comb || a.deferred != 1) return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave), 0, stream, a, p.R, p.n_rb);
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave * p.wg_waves), 0, stream, a, p.R, p.n_rb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !comb) return e;
     const int64_t rows = (int64_t)a.B * a.G * p.n_rb * p.row_block;
