@@ -387,7 +387,7 @@ struct Pending {
     int seg;          // arrival counter index
     int p_first;      // first workgroup holding a piece of the segment
     int npieces;
-    long long off;    // the segment's first work unit
+    long long off;    // position of the segment's first row in the work split
     int64_t qrow0;    // output row of the segment's first query row
     int row0;         // first query row of the segment within its KV head
 };
@@ -1286,33 +1286,47 @@ __device__ __forceinline__ float sum_x32(float x)
 }
 
 // ---------------------------------------------------------------------------
-// Work split of the matrix-core pass: the W work units (cache rows of all
-// segments, in order) are cut into P chunks with fixed boundaries, chunk
-// c = [c W / P, (c + 1) W / P) taken by workgroup c; with fewer units than
-// workgroups, only the first W workgroups take one unit each, so no chunk
-// is empty (a merge waits for every chunk between a segment's first and
-// last).  A piece is a chunk's part of one segment; its partial lives in a
-// slot of the chunk, and merges go in chunk order.
+// Work split of the matrix-core pass.  Work is counted in cost units: a
+// segment (sequence b, KV head g, row block rb) with L > 0 cache rows costs
+// kPieceCost + L -- its rows plus what starting a piece of it costs a
+// workgroup (loading its queries, filling the load pipeline, writing its
+// result).  All segments end to end span V cost units, cut into P chunks
+// with fixed boundaries, chunk c = [c V / P, (c + 1) V / P), taken by
+// workgroup c; with V < P only the first V workgroups take one unit each.
+// A chunk that holds the start of a segment (so one more piece) thereby
+// gets fewer rows.  A piece is a chunk's part of one segment's rows; its
+// partial lives in a slot of the chunk, and merges go in chunk order.  A
+// chunk may hold only start cost and no rows: it has no piece, and no
+// segment counts it among its pieces (every chunk between a segment's first
+// and last row holds rows of it).
 //
 // (A guided deal -- most of each share static, the rest in small chunks
 // handed out by a global counter -- was measured slower on every workload:
 // thousands of device-scope atomics on one address serialise.)
 // ---------------------------------------------------------------------------
+constexpr int kPieceCost = 64;   // rows a workgroup could stream while starting a piece (~3 us, measured)
+
 struct ChunkMap {
-    long long W;
+    long long V;
     int P;
 
-    __device__ __forceinline__ long long start(int c) const { return (long long)c * W / P; }
-    // the chunk holding unit x, 0 <= x < W
-    __device__ __forceinline__ int of(long long x) const { return (int)(((x + 1) * P - 1) / W); }
+    __device__ __forceinline__ long long start(int c) const { return (long long)c * V / P; }
+    // the chunk holding cost unit x, 0 <= x < V
+    __device__ __forceinline__ int of(long long x) const { return (int)(((x + 1) * P - 1) / V); }
 };
 
-__device__ __forceinline__ ChunkMap make_map(long long W, int P)
+__device__ __forceinline__ ChunkMap make_map(long long V, int P)
 {
     ChunkMap m;
-    m.W = W;
-    m.P = W < P ? (int)W : P;
+    m.V = V;
+    m.P = V < P ? (int)V : P;
     return m;
+}
+
+// Cost units of one segment of a sequence with L clamped rows.
+__device__ __forceinline__ uint32_t seg_cost(int L)
+{
+    return L > 0 ? (uint32_t)(L + kPieceCost) : 0u;
 }
 
 // Partial slots of the matrix-core pass: two per chunk (slot 0 for the
@@ -1339,40 +1353,90 @@ __device__ __forceinline__ int lens_at(const Args& a, const int* lens, int b)
     return b < kLensWindow ? lens[b] : clamp_len(a.seq_lens, b, a.T);
 }
 
-// Sum of the clamped lengths (every lane gets it).
-__device__ __forceinline__ long long total_rows(const Args& a, const int* lens)
+// Cost units of one segment of every sequence, summed (every lane gets it).
+__device__ __forceinline__ long long total_cost(const Args& a, const int* lens)
 {
     const int lane = threadIdx.x & (kWave - 1);
     long long tot = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        tot += wave_sum_u32(b < a.B ? (uint32_t)lens_at(a, lens, b) : 0u);
+        tot += wave_sum_u32(b < a.B ? seg_cost(lens_at(a, lens, b)) : 0u);
     }
     return tot;
 }
 
-// First sequence whose units reach past unit x, and the units before it.
+// First sequence whose cost units reach past unit x, and the units before it.
 __device__ __forceinline__ void locate(const Args& a, const int* lens, int units, long long x, int& first_b,
-                                       long long& first_e)
+                                       long long& first_v)
 {
     const int lane = threadIdx.x & (kWave - 1);
     long long carry = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        const uint32_t L = b < a.B ? (uint32_t)lens_at(a, lens, b) : 0u;
-        const uint32_t incl = wave_incl_scan_u32(L, lane);
+        const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b)) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(c, lane);
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
         if (hit) {
             const int f = __builtin_ctzll(hit);
             first_b = b0 + f;
-            first_e = (carry + __shfl(incl - L, f)) * units;
+            first_v = (carry + __shfl(incl - c, f)) * units;
             return;
         }
         carry += __shfl(incl, kWave - 1);
     }
     first_b = a.B;
-    first_e = carry * units;
+    first_v = carry * units;
 }
+
+// Yields the pieces of the chunk [vA, vE) (cost units) in order; a piece's
+// `off` is the cost-unit position of its segment's first row.
+struct CostPieceIter {
+    long long vA, vE, Vb;   // the chunk; cost units before sequence b
+    int b, k, units, n_rb;
+
+    __device__ __forceinline__ void init(long long vA_, long long vE_, int fb, long long fv, int G, int n_rb_)
+    {
+        vA = vA_;
+        vE = vE_;
+        Vb = fv;
+        b = fb;
+        k = -1;
+        n_rb = n_rb_;
+        units = G * n_rb_;
+    }
+
+    __device__ __forceinline__ bool next(const Args& a, const int* lens, Piece& pc)
+    {
+        while (b < a.B && Vb < vE) {
+            const int Lb = lens_at(a, lens, b);
+            if (Lb > 0) {
+                const long long sc = (long long)Lb + kPieceCost;
+                if (k < 0) k = vA > Vb ? (int)((vA - Vb) / sc) : 0;
+                while (k < units) {
+                    const long long vfirst = Vb + k * sc + kPieceCost;
+                    if (vfirst - kPieceCost >= vE) return false;
+                    const long long ta = vA > vfirst ? vA - vfirst : 0;
+                    const long long tb = vE - vfirst < Lb ? vE - vfirst : Lb;
+                    const int kk = k++;
+                    if (tb > ta) {
+                        pc.b = b;
+                        pc.g = kk / n_rb;
+                        pc.rb = kk % n_rb;
+                        pc.ta = (int)ta;
+                        pc.tb = (int)tb;
+                        pc.L = Lb;
+                        pc.off = vfirst;
+                        return true;
+                    }
+                }
+            }
+            Vb += (long long)units * seg_cost(Lb);
+            ++b;
+            k = -1;
+        }
+        return false;
+    }
+};
 
 // One piece of segment (b, g, rb) -- cache rows [ta, tb) for the RB = 16 NB
 // query rows RB rb .. RB rb + RB - 1 -- streamed in 16-row tiles with the
@@ -1782,19 +1846,19 @@ decode_mfa(const Args a, const int R, const int n_rb)
     for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
     const int units = a.G * n_rb;
-    const long long W = total_rows(a, sm.lens) * units;
-    if (W == 0) return;
-    const ChunkMap cm = make_map(W, P);
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer units than workgroups
-    const long long A = cm.start(chunk), E = cm.start(chunk + 1);
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
     int fb;
-    long long fe;
-    locate(a, sm.lens, units, A, fb, fe);
-    PieceIter it;
-    it.init_range(A, E, fb, fe, a.G, n_rb);
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
     Piece pc;
-    while (it.next(a, sm.lens, 0, pc)) {
+    while (it.next(a, sm.lens, pc)) {
         Pending pd;
         if (mfa_piece<D, NB, SRC, KV8>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
@@ -2026,19 +2090,19 @@ decode_mfw(const Args a, const int R, const int n_rb)
     for (int i = tid; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     __syncthreads();
     const int units = a.G * n_rb;
-    const long long W = total_rows(a, sm.lens) * units;
-    if (W == 0) return;
-    const ChunkMap cm = make_map(W, P);
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer units than workgroups
-    const long long A = cm.start(chunk), E = cm.start(chunk + 1);
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
     int fb;
-    long long fe;
-    locate(a, sm.lens, units, A, fb, fe);
-    PieceIter it;
-    it.init_range(A, E, fb, fe, a.G, n_rb);
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
     Piece pc;
-    while (it.next(a, sm.lens, 0, pc)) {
+    while (it.next(a, sm.lens, pc)) {
         Pending pd;
         if (mfw_piece<D, NW>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
             __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores complete at device scope
@@ -2078,17 +2142,18 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
     if (row >= R) return;
     const int L = clamp_len(a.seq_lens, b, a.T);
     if (L == 0) return;
-    // units before sequence b, and in total (every wave of the grid agrees)
+    // cost units before sequence b, and in total (every wave of the grid agrees)
     long long before = 0, tot = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int bb = b0 + lane;
-        const uint32_t Lb = bb < a.B ? (uint32_t)clamp_len(a.seq_lens, bb, a.T) : 0u;
-        tot += wave_sum_u32(Lb);
-        before += wave_sum_u32(bb < b ? Lb : 0u);
+        const uint32_t c = bb < a.B ? seg_cost(clamp_len(a.seq_lens, bb, a.T)) : 0u;
+        tot += wave_sum_u32(c);
+        before += wave_sum_u32(bb < b ? c : 0u);
     }
     const long long units = (long long)a.G * n_rb;
     const ChunkMap cm = make_map(tot * units, P);
-    const long long off = before * units + ((long long)g * n_rb + rb) * L;
+    // the cost-unit position of the segment's first row
+    const long long off = before * units + ((long long)g * n_rb + rb) * ((long long)L + kPieceCost) + kPieceCost;
     const int c_first = cm.of(off);
     const int npieces = cm.of(off + L - 1) - c_first + 1;
     if (npieces == 1) return;                 // written by its piece
