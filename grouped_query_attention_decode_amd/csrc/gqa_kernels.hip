@@ -1194,6 +1194,20 @@ decode_mqk(const Args a, const int R, const int n_rb)
 // bf16, and accumulation is fp32.
 // ---------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Four bf16 of one column of a row-major bf16 block in LDS, four rows apart
+// in the A-operand order of v_mfma_f32_16x16x16_bf16, by the gfx950 LDS
+// transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte pieces addressed by lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group, in that order.  So when
+// lane (kg, s) of the wave addresses row 4 kg + s / 4, columns 4 (s % 4) ..
+// 4 (s % 4) + 3 of a 16 x 16 block, lane (kg, col) receives column col of
+// rows 4 kg .. 4 kg + 3.  p must be 8-byte aligned.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p)
+{
+    typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+}
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // The running max is moved only when a tile's max exceeds it by more than
@@ -1244,7 +1258,7 @@ constexpr int kSrcPaged = 2;    // page pool [num_pages, G, page_size, D] and a 
 
 template <int D>
 struct MfaShared {
-    static constexpr int SE = D + 16;   // LDS row stride (bf16): the four row groups of a read hit distinct banks
+    static constexpr int SE = D + 16;   // LDS row stride (bf16): the 32-byte pieces of eight consecutive rows cover all 64 banks
     alignas(16) uint16_t vt[16 * SE];   // V tile, row-major
     int lens[kLensWindow];              // clamped seq_lens[i]
     int pages[kPageWindow];             // paged cache: physical pages of the current row window
@@ -1672,11 +1686,12 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             ph[nb] = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
             pl[nb] = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
         }
-        const uint16_t* vr = sm.vt + 4 * kg * SE + col;
+        // lane (kg, col) addresses row 4 kg + col / 4, columns 4 (col % 4) ..
+        // of each 16-column block and receives V^T[col][4 kg .. 4 kg + 3]
+        const uint16_t* vr = sm.vt + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const s16x4_t va = {(short)vr[16 * c], (short)vr[SE + 16 * c], (short)vr[2 * SE + 16 * c],
-                                (short)vr[3 * SE + 16 * c]};
+            const s16x4_t va = lds_read_tr16(vr + 16 * c);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[nb], acc[nb][c], 0, 0, 0);
@@ -2009,11 +2024,10 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
         const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
         const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
         const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
-        const uint16_t* vr = sm.vt[buf] + 4 * kg * SE + col;
+        const uint16_t* vr = sm.vt[buf] + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const s16x4_t va = {(short)vr[16 * c], (short)vr[SE + 16 * c], (short)vr[2 * SE + 16 * c],
-                                (short)vr[3 * SE + 16 * c]};
+            const s16x4_t va = lds_read_tr16(vr + 16 * c);
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[c], 0, 0, 0);
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[c], 0, 0, 0);
         }
