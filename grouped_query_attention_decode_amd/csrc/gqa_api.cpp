@@ -135,10 +135,10 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
     // then one wave on each of the four SIMDs of a compute unit.  So does an
     // fp8 cache (half the bytes per tile for the same arithmetic).
-    // More than 16 query rows of a plain bf16 cache: workgroups of
-    // row_block / 16 waves sharing each K/V tile through LDS, two waves per
-    // SIMD.
-    p->wg_waves = (p->path == gqa::Path::MFMA && !p->kv_fp8 && src == 0 && p->row_block >= 32)
+    // More than 32 query rows of a plain bf16 cache: workgroups of four
+    // waves sharing each K/V tile through LDS, two waves per SIMD (up to 32
+    // rows one wave carrying two blocks measured faster).
+    p->wg_waves = (p->path == gqa::Path::MFMA && !p->kv_fp8 && src == 0 && p->row_block >= 64)
                       ? p->row_block / 16 : 1;
     int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;
     if (p->wg_waves > 1) want = gqa::kMultiWaveWavesPerCU / p->wg_waves;

@@ -1900,21 +1900,22 @@ decode_mfa(const Args a, const int R, const int n_rb)
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core pass for groups of more than 16 query rows.  A workgroup of NW
-// waves (NW = 2 or 4) owns segments of 16 NW query rows; wave w computes
-// rows 16 w .. 16 w + 15 as decode_mfa computes one block, and the NW waves
-// share every K/V tile: the workgroup loads it once (each thread a share of
-// its 16-byte chunks, two tiles ahead in registers) and stages it in LDS,
-// double-buffered, one barrier per tile.  Compared with one wave carrying
-// all the blocks, the blocks' arithmetic runs on NW SIMDs at once, and a
-// split segment's merge is shared by the NW waves too.
+// Matrix-core pass for groups of more than 32 query rows.  A workgroup of NW
+// waves (NW = 4) owns segments of 16 NW query rows; wave w computes rows
+// 16 w .. 16 w + 15, and the NW waves share every K/V tile of 32 cache rows:
+// the workgroup loads it once (each thread a share of its 16-byte chunks,
+// one tile ahead in registers) and stages it in LDS, double-buffered, one
+// barrier per tile.  Compared with one wave carrying all the blocks, the
+// blocks' arithmetic runs on NW SIMDs at once, and a split segment's merge
+// is shared by the NW waves too.
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 struct MfwShared {
+    static constexpr int TR = 32;       // cache rows per tile
     static constexpr int SK = D + 8;    // K row stride (bf16): the 16 rows of an A-operand read hit distinct banks
     static constexpr int SE = D + 16;   // V row stride, as in MfaShared
-    alignas(16) uint16_t kt[2][16 * SK];
-    alignas(16) uint16_t vt[2][16 * SE];
+    alignas(16) uint16_t kt[2][TR * SK];
+    alignas(16) uint16_t vt[2][TR * SE];
     int lens[kLensWindow];              // clamped seq_lens[i]
     int merge;                          // 1 when this workgroup arrived last for the current piece
 };
@@ -1927,9 +1928,10 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
     constexpr int NC = D / 16;
     constexpr int SK = MfwShared<D, NW>::SK;
     constexpr int SE = MfwShared<D, NW>::SE;
+    constexpr int TR = MfwShared<D, NW>::TR;
     constexpr int CPR = D / 8;           // 16-byte chunks per cache row
     constexpr int NT = kWave * NW;       // threads of the workgroup
-    constexpr int NCH = (16 * CPR + NT - 1) / NT;   // K chunks (and V chunks) per thread per tile
+    constexpr int NCH = (TR * CPR + NT - 1) / NT;   // K chunks (and V chunks) per thread per tile
     constexpr int RB = 16 * NW;
 
     const int tid = threadIdx.x;
@@ -1944,7 +1946,7 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
     const bool live = r < R;
     const int last = live ? pc.L - a.sq + (r % a.sq) : -1;
     // with D = 64 and four waves half of the threads have no chunk
-    auto has = [&](int j) { return (16 * CPR) % NT == 0 || tid + NT * j < 16 * CPR; };
+    auto has = [&](int j) { return (TR * CPR) % NT == 0 || tid + NT * j < TR * CPR; };
 
     uint4 qb[NK];
     {
@@ -1969,7 +1971,7 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
-            const int c = min(tid + NT * j, 16 * CPR - 1);
+            const int c = min(tid + NT * j, TR * CPR - 1);
             const int64_t off = ((int64_t)min(t0 + c / CPR, tb - 1) * D + (c % CPR) * 8) * 2;
             kk[j] = load16_stream(kbase + off);
             vv[j] = load16_stream(vbase + off);
@@ -1984,24 +1986,35 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
             *reinterpret_cast<uint4*>(&sm.vt[buf][(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
         }
     };
+    // A tile is two 16-row halves h: scores S^T_h = K_h Q^T on
+    // v_mfma_f32_16x16x32_bf16 (lane (kg, col) gets rows 4 kg .. 4 kg + 3 of
+    // half h for query row col), then one online-softmax step over the 32
+    // rows, and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with its k index
+    // 8 kg + i standing for tile row 16 (i / 4) + 4 kg + i % 4 -- the rows
+    // lane (kg, col) already holds the weights of, and the rows the two
+    // transpose reads of V deliver.
     auto compute = [&](int buf, int t0) {
-        uint4 kk[NK];
+        f32x4_t s4[2];
 #pragma unroll
-        for (int s = 0; s < NK; ++s)
-            kk[s] = *reinterpret_cast<const uint4*>(&sm.kt[buf][col * SK + kdim0<D, false>(kg, s)]);
-        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int h = 0; h < 2; ++h) {
+            uint4 kk[NK];
 #pragma unroll
-        for (int s = 0; s < NK; ++s)
-            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
-                                                         __builtin_bit_cast(bf16x8_t, qb[s]), s4, 0, 0, 0);
-        const bool full = t0 + 16 <= tb && t0 + 15 <= pc.L - a.sq;
-        float sc[4];
+            for (int s = 0; s < NK; ++s)
+                kk[s] = *reinterpret_cast<const uint4*>(&sm.kt[buf][(16 * h + col) * SK + kdim0<D, false>(kg, s)]);
+            s4[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < NK; ++s)
+                s4[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
+                                                                __builtin_bit_cast(bf16x8_t, qb[s]), s4[h], 0, 0, 0);
+        }
+        const bool full = t0 + TR <= tb && t0 + TR - 1 <= pc.L - a.sq;
+        float sc[8];
         float mx = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int t = t0 + 4 * kg + jj;
-            sc[jj] = (full || (t < tb && t <= last)) ? s4[jj] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sc[jj]);
+        for (int i = 0; i < 8; ++i) {
+            const int t = t0 + 16 * (i >> 2) + 4 * kg + (i & 3);
+            sc[i] = (full || (t < tb && t <= last)) ? s4[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[i]);
         }
         mx = max_x32(max_x16(mx));
         const bool need = mx > m_run + kSlack;
@@ -2012,45 +2025,52 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
 #pragma unroll
             for (int c = 0; c < NC; ++c) acc[c] *= al;
         }
-        float pv[4];
+        float pv[8];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            pv[jj] = (!full && sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run);
-            l_run += pv[jj];
+        for (int i = 0; i < 8; ++i) {
+            pv[i] = (!full && sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m_run);
+            l_run += pv[i];
         }
-        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
-        const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
-        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
-        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
-        const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
-        const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+        // p = hi + lo, both bf16
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hw[q] = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+            lw[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(hw[q] << 16),
+                                pv[2 * q + 1] - __uint_as_float(hw[q] & 0xFFFF0000u));
+        }
+        const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         const uint16_t* vr = sm.vt[buf] + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const s16x4_t va = lds_read_tr16(vr + 16 * c);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[c], 0, 0, 0);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[c], 0, 0, 0);
+            const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * c));
+            const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * SE + 16 * c));
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[c], 0, 0, 0);
         }
     };
 
-    // Tile i is computed from LDS buffer i & 1 while tile i + 1 is staged
-    // into the other buffer and tile i + 2 is in flight; the barrier after
-    // each tile orders both for the next.
+    // Iteration i stages tile i + 1 (loaded during iteration i - 1) into
+    // LDS buffer (i + 1) & 1, issues the loads of tile i + 2 into the
+    // registers just freed, and computes tile i from buffer i & 1; the
+    // barrier after each tile orders the staging for the next.
     {
-        uint4 kr[3][NCH], vr[3][NCH];
-        const int ntile = (tb - ta + 15) / 16;
+        uint4 kr[2][NCH], vr[2][NCH];
+        const int ntile = (tb - ta + TR - 1) / TR;
         load_tile(ta, kr[0], vr[0]);
-        load_tile(ta + 16, kr[1], vr[1]);
+        load_tile(ta + TR, kr[1], vr[1]);
         stage(0, kr[0], vr[0]);
         __syncthreads();
-        for (int it = 0; it < ntile; it += 3) {
+        for (int it = 0; it < ntile; it += 2) {
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 const int i = it + u;
                 if (i >= ntile) break;
-                load_tile(ta + 16 * (i + 2), kr[(u + 2) % 3], vr[(u + 2) % 3]);
-                if (i + 1 < ntile) stage((i + 1) & 1, kr[(u + 1) % 3], vr[(u + 1) % 3]);
-                compute(i & 1, ta + 16 * i);
+                if (i + 1 < ntile) stage((i + 1) & 1, kr[1 - u], vr[1 - u]);
+                load_tile(ta + TR * (i + 2), kr[u], vr[u]);
+                compute(i & 1, ta + TR * i);
                 __syncthreads();
             }
         }
@@ -2264,7 +2284,6 @@ static DecodeFn pick(const Plan& p)
 {
     if (p.path == Path::MFMA && p.wg_waves > 1) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
-        if (p.wg_waves == 2) return p.D == 64 ? decode_mfw<64, 2> : decode_mfw<128, 2>;
         if (p.wg_waves == 4) return p.D == 64 ? decode_mfw<64, 4> : decode_mfw<128, 4>;
         return nullptr;
     }

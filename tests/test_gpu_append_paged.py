@@ -131,7 +131,14 @@ def test_paged_matches_oracle_and_decode(gqa, orc, case):
     assert _err(got, want) <= TOL
     ref = gqa.decode(q, x["k"].cuda(), x["v"].cuda(), sl)
     torch.cuda.synchronize()
-    assert torch.equal(got, ref)
+    if (H // G) * sq <= 32:
+        # the same one-wave kernel over the same rows: the same bits
+        assert torch.equal(got, ref)
+    else:
+        # a contiguous cache of more than 32 query rows per KV head runs on
+        # 32-row tiles shared by a multi-wave workgroup, the paged kernel on
+        # 16-row tiles: the same sums in another order
+        assert (got - ref).abs().max().item() <= 2e-5
 
 
 def test_paged_piece_longer_than_page_window(gqa, orc):
