@@ -1216,11 +1216,19 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // tiles skip the rescale.
 constexpr float kSlack = 8.0f;
 
-// K/V tiles held in registers per wave: 3 (two in flight) measured best; with
-// four 16-row query blocks the accumulators need the room, so 2.
-// fp8 tiles are half the bytes, so twice as many are kept in flight.
+// Cache rows per tile of the one-wave matrix-core pass: 32 (two 16-row
+// halves sharing one softmax step and K = 32 weighted-sum products); 16 when
+// four query blocks' accumulators and operands leave no room for 32-row
+// tiles in flight.
+template <int NB>
+constexpr int mfa_tile_rows() { return NB >= 4 ? 16 : 32; }
+
+// K/V tiles held in registers per wave: two 32-row tiles (one in flight
+// while one is computed: 16 KB of a bf16 cache), or two 16-row tiles with
+// four query blocks; fp8 tiles are half the bytes, so one more is kept in
+// flight.
 template <int NB, bool KV8>
-constexpr int mfa_buffers() { return KV8 ? (NB >= 4 ? 3 : 5) : (NB >= 4 ? 2 : 3); }
+constexpr int mfa_buffers() { return KV8 ? 3 : 2; }
 
 // Head-dim element where the 8 elements of score-product step s start for
 // k group kg (the order of the reduction over d is free as long as K and Q
@@ -1259,7 +1267,7 @@ constexpr int kSrcPaged = 2;    // page pool [num_pages, G, page_size, D] and a 
 template <int D>
 struct MfaShared {
     static constexpr int SE = D + 16;   // LDS row stride (bf16): the 32-byte pieces of eight consecutive rows cover all 64 banks
-    alignas(16) uint16_t vt[16 * SE];   // V tile, row-major
+    alignas(16) uint16_t vt[32 * SE];   // V tile (up to 32 rows), row-major
     int lens[kLensWindow];              // clamped seq_lens[i]
     int pages[kPageWindow];             // paged cache: physical pages of the current row window
 };
@@ -1470,7 +1478,7 @@ struct CostPieceIter {
 };
 
 // One piece of segment (b, g, rb) -- cache rows [ta, tb) for the RB = 16 NB
-// query rows RB rb .. RB rb + RB - 1 -- streamed in 16-row tiles with the
+// query rows RB rb .. RB rb + RB - 1 -- streamed in 32-row tiles with the
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
@@ -1484,8 +1492,10 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     constexpr int ES = KV8 ? 1 : 2;      // bytes per cache element (fp8 codes or bf16)
     constexpr int EPC = 16 / ES;         // cache elements per 16-byte chunk
     constexpr int CPR = D / EPC;         // 16-byte chunks per cache row
-    constexpr int NLV = 16 * CPR / kWave;   // V loads per lane per tile
-    constexpr int NLK = KV8 ? D / 64 : NK;  // K loads per lane per tile
+    constexpr int TR = mfa_tile_rows<NB>();  // cache rows per tile
+    constexpr int NH = TR / 16;              // 16-row halves of a tile
+    constexpr int NLV = TR * CPR / kWave;   // V loads per lane per tile
+    constexpr int NLK = KV8 ? D / 64 : NK;  // K loads per lane per half tile
     constexpr int RB = 16 * NB;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -1539,12 +1549,17 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     int wpage0 = 0;                      // paged: first page of the LDS window
     bool wnew = false;                   // append: the window holds the new tokens' rows
     int tend = tb;                       // end of the current row window
-    // paged: pages of the rows the next load_tile reads (K row, V rows),
-    // looked up one tile ahead so the LDS latency hides behind a compute_tile
-    int pgk = 0, pgv[NLV];
+    // paged: pages of the rows the next load_tile reads (the K rows of both
+    // halves, the V rows), looked up one tile ahead so the LDS latency hides
+    // behind a compute_tile
+    int pgk[NH], pgv[NLV];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) pgk[h] = 0;
     auto lookup = [&](int t0) {
         if constexpr (SRC == kSrcPaged) {
-            pgk = sm.pages[(min(t0 + col, tend - 1) >> a.page_shift) - wpage0];
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+                pgk[h] = sm.pages[(min(t0 + 16 * h + col, tend - 1) >> a.page_shift) - wpage0];
 #pragma unroll
             for (int j = 0; j < NLV; ++j)
                 pgv[j] = sm.pages[(min(t0 + (lane + kWave * j) / CPR, tend - 1) >> a.page_shift) - wpage0];
@@ -1569,32 +1584,46 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         }
     };
 
-    // Rows past the window's end re-read its last row (valid): their weights
-    // are exactly 0, so no row at or beyond the end is read and no branch
-    // guards the loads.  K: lane (kg, col) loads row col, elements
+    // A tile is TR cache rows, NH halves h of 16.  Rows past the window's
+    // end re-read its last row (valid): their weights are exactly 0, so no
+    // row at or beyond the end is read and no branch guards the loads.
+    // K: lane (kg, col) loads row 16 h + col of each half, elements
     // 8 kg + 32 s ..; V: chunk c = lane + 64 j is row c / CPR, elements
-    // 8 (c % CPR) ..
+    // EPC (c % CPR) ..
     auto load_tile = [&](int t0, uint4* kk, uint4* vv) {
-        const char* kr = row_addr(a.k, a.k_new, pgk, min(t0 + col, tend - 1));
-        // bf16: elements kdim0(kg, s) .. + 7 for step s; fp8: 16 codes from
-        // element 16 kg + 64 h (steps 2h and 2h + 1)
 #pragma unroll
-        for (int s = 0; s < NLK; ++s)
-            kk[s] = load16_stream(kr + (KV8 ? 16 * kg + 64 * s : 2 * kdim0<D, KV8>(kg, s)));
+        for (int h = 0; h < NH; ++h) {
+            const char* kr = row_addr(a.k, a.k_new, pgk[h], min(t0 + 16 * h + col, tend - 1));
+            // bf16: elements kdim0(kg, s) .. + 7 for step s; fp8: 16 codes from
+            // element 16 kg + 64 s (steps 2s and 2s + 1)
+#pragma unroll
+            for (int s = 0; s < NLK; ++s)
+                kk[h * NLK + s] = load16_stream(kr + (KV8 ? 16 * kg + 64 * s : 2 * kdim0<D, KV8>(kg, s)));
+        }
 #pragma unroll
         for (int j = 0; j < NLV; ++j) {
             const int c = lane + kWave * j;
             vv[j] = load16_stream(row_addr(a.v, a.v_new, pgv[j], min(t0 + c / CPR, tend - 1)) + (c % CPR) * 16);
         }
-        lookup(t0 + 16);
+        lookup(t0 + TR);
     };
 
+    // Scores per half, S^T_h = K_h Q^T on v_mfma_f32_16x16x32_bf16 (lane
+    // (kg, col) gets rows 4 kg .. 4 kg + 3 of half h for query row col), one
+    // online-softmax step over the tile's rows, then O^T += V^T P^T: for a
+    // 32-row tile on v_mfma_f32_16x16x32_bf16 whose k index 8 kg + i stands
+    // for tile row 16 (i / 4) + 4 kg + i % 4 -- the rows whose weights lane
+    // (kg, col) holds, and the rows the two LDS transpose reads of V deliver
+    // to it; for a 16-row tile on v_mfma_f32_16x16x16_bf16 (k index 4 kg + i
+    // is row 4 kg + i).
     auto compute_tile = [&](int t0, const uint4* kin, const uint4* vv) {
-        uint4 kk[NK];
+        uint4 kk[NH][NK];
         if constexpr (KV8) {
             // 16 fp8 codes -> two 8-element bf16 operands (exact)
 #pragma unroll
-            for (int h = 0; h < NLK; ++h) fp8x16_to_bf16(kin[h], kk[2 * h], kk[2 * h + 1]);
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int s = 0; s < NLK; ++s) fp8x16_to_bf16(kin[h * NLK + s], kk[h][2 * s], kk[h][2 * s + 1]);
 #pragma unroll
             for (int j = 0; j < NLV; ++j) {
                 const int c = lane + kWave * j;
@@ -1606,7 +1635,9 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < NK; ++s) kk[s] = kin[s];
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int s = 0; s < NK; ++s) kk[h][s] = kin[h * NLK + s];
 #pragma unroll
             for (int j = 0; j < NLV; ++j) {
                 const int c = lane + kWave * j;
@@ -1616,11 +1647,14 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         if constexpr (SRC == kSrcAppend) {
             // the first row block's pieces store the new tokens' rows into the cache
             if (wnew && pc.rb == 0) {
-                const int tk = t0 + col;
-                if (tk >= la && tk < tend) {
-                    char* kr = static_cast<char*>(const_cast<void*>(a.k)) + (slab + (int64_t)tk * D) * 2 + 16 * kg;
 #pragma unroll
-                    for (int s = 0; s < NK; ++s) *reinterpret_cast<uint4*>(kr + 64 * s) = kk[s];
+                for (int h = 0; h < NH; ++h) {
+                    const int tk = t0 + 16 * h + col;
+                    if (tk >= la && tk < tend) {
+                        char* kr = static_cast<char*>(const_cast<void*>(a.k)) + (slab + (int64_t)tk * D) * 2 + 16 * kg;
+#pragma unroll
+                        for (int s = 0; s < NK; ++s) *reinterpret_cast<uint4*>(kr + 64 * s) = kk[h][s];
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < NLV; ++j) {
@@ -1632,33 +1666,38 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
                 }
             }
         }
-        s16x4_t ph[NB], pl[NB];
+        uint32_t hw[NB][2 * NH], lw[NB][2 * NH];   // weights p = hi + lo, bf16 pairs
         // no row of the tile is past the window or after the first new token
-        const bool full = t0 + 16 <= tend && t0 + 15 <= pc.L - a.sq;
+        const bool full = t0 + TR <= tend && t0 + TR - 1 <= pc.L - a.sq;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t s4[NH];
 #pragma unroll
-            for (int s = 0; s < NK; ++s)
-                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[s]),
-                                                             __builtin_bit_cast(bf16x8_t, qb[nb][s]), s4, 0, 0, 0);
-            float sc[4];
+            for (int h = 0; h < NH; ++h) {
+                s4[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < NK; ++s)
+                    s4[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[h][s]),
+                                                                    __builtin_bit_cast(bf16x8_t, qb[nb][s]), s4[h], 0, 0,
+                                                                    0);
+            }
+            float sc[4 * NH];
             float mx = -INFINITY;
             if (full) {
                 // every row of the tile is visible to every new token (rows of
                 // padding query rows are not masked either: their results are
                 // never stored)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    sc[jj] = s4[jj] * score_scale;
-                    mx = fmaxf(mx, sc[jj]);
+                for (int i = 0; i < 4 * NH; ++i) {
+                    sc[i] = s4[i >> 2][i & 3] * score_scale;
+                    mx = fmaxf(mx, sc[i]);
                 }
             } else {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int t = t0 + 4 * kg + jj;
-                    sc[jj] = (t < tend && t <= last[nb]) ? s4[jj] * score_scale : -INFINITY;
-                    mx = fmaxf(mx, sc[jj]);
+                for (int i = 0; i < 4 * NH; ++i) {
+                    const int t = t0 + 16 * (i >> 2) + 4 * kg + (i & 3);
+                    sc[i] = (t < tend && t <= last[nb]) ? s4[i >> 2][i & 3] * score_scale : -INFINITY;
+                    mx = fmaxf(mx, sc[i]);
                 }
             }
             mx = max_x32(max_x16(mx));
@@ -1671,31 +1710,46 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
                 for (int c = 0; c < NC; ++c) acc[nb][c] *= al;
             }
-            float pv[4];
+            float pv[4 * NH];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int i = 0; i < 4 * NH; ++i) {
                 // in a full tile every score is finite and so is m_run
-                pv[jj] = (!full && sc[jj] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - m_run[nb]);
-                l_run[nb] += pv[jj];
+                pv[i] = (!full && sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m_run[nb]);
+                l_run[nb] += pv[i];
             }
-            // p = hi + lo, both bf16
-            const uint32_t h01 = pack_bf16x2(pv[0], pv[1]);
-            const uint32_t h23 = pack_bf16x2(pv[2], pv[3]);
-            const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
-            const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
-            ph[nb] = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
-            pl[nb] = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+#pragma unroll
+            for (int q = 0; q < 2 * NH; ++q) {
+                hw[nb][q] = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+                lw[nb][q] = pack_bf16x2(pv[2 * q] - __uint_as_float(hw[nb][q] << 16),
+                                        pv[2 * q + 1] - __uint_as_float(hw[nb][q] & 0xFFFF0000u));
+            }
         }
-        // lane (kg, col) addresses row 4 kg + col / 4, columns 4 (col % 4) ..
-        // of each 16-column block and receives V^T[col][4 kg .. 4 kg + 3]
+        // lane (kg, col) addresses row 4 kg + col / 4 (of each half), columns
+        // 4 (col % 4) .. of each 16-column block and receives
+        // V^T[col][4 kg .. 4 kg + 3] of the half
         const uint16_t* vr = sm.vt + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const s16x4_t va = lds_read_tr16(vr + 16 * c);
+            const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * c));
+            if constexpr (NH == 2) {
+                const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * SE + 16 * c));
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[nb], acc[nb][c], 0, 0, 0);
-                acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[nb], acc[nb][c], 0, 0, 0);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[nb][0], hw[nb][1], hw[nb][2], hw[nb][3]));
+                    const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[nb][0], lw[nb][1], lw[nb][2], lw[nb][3]));
+                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[nb][c], 0, 0, 0);
+                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[nb][c], 0, 0, 0);
+                }
+            } else {
+                const s16x4_t va = __builtin_bit_cast(s16x4_t, v0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(hw[nb][0], hw[nb][1]));
+                    const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(lw[nb][0], lw[nb][1]));
+                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[nb][c], 0, 0, 0);
+                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[nb][c], 0, 0, 0);
+                }
             }
         }
     };
@@ -1723,19 +1777,19 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         }
         lookup(w0);
         constexpr int NBUF = mfa_buffers<NB, KV8>();
-        uint4 kb[NBUF][NLK], vb[NBUF][NLV];
+        uint4 kb[NBUF][NH * NLK], vb[NBUF][NLV];
         int t0 = w0;
-        const int ntile = (tend - w0 + 15) / 16;
+        const int ntile = (tend - w0 + TR - 1) / TR;
 #pragma unroll
-        for (int u = 0; u < NBUF - 1; ++u) load_tile(t0 + 16 * u, kb[u], vb[u]);
+        for (int u = 0; u < NBUF - 1; ++u) load_tile(t0 + TR * u, kb[u], vb[u]);
         for (int it = 0; it < ntile; it += NBUF) {
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
                 if (it + u >= ntile) break;
                 const int nxt = (u + NBUF - 1) % NBUF;
-                load_tile(t0 + 16 * (NBUF - 1), kb[nxt], vb[nxt]);
+                load_tile(t0 + TR * (NBUF - 1), kb[nxt], vb[nxt]);
                 compute_tile(t0, kb[u], vb[u]);
-                t0 += 16;
+                t0 += TR;
             }
         }
     }

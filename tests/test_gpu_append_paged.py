@@ -5,8 +5,12 @@ in one pass) and gqa_decode_paged (page pool + block table).
 Tolerances as for gqa_decode (bf16 inputs, fp32 accumulation: 2e-3 max
 abs).  The cache rows an append writes are compared bit for bit; a paged
 decode is also compared bit for bit with gqa_decode on the cache it
-describes (same plan, same arithmetic), an append to within 2e-5 (its
-tiles restart at the first new row)."""
+describes where both run the same kernel on the same tiles, otherwise to
+within REORDER_TOL, as is an append (its tiles restart at the first new
+row).  REORDER_TOL: the same sums in another order -- each weight p is
+carried as bf16 hi + lo (about 16 significant bits), so a change in the
+last bit of a score can move a weight by ~2^-16 of itself and an output by
+~1e-5; 1e-4 bounds that with room, 20x under TOL."""
 import math
 
 import numpy as np
@@ -17,6 +21,7 @@ import gqa_inputs as gi
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
+REORDER_TOL = 1e-4
 
 
 @pytest.fixture(scope="module")
@@ -72,7 +77,7 @@ def test_append_matches_oracle_and_decode(gqa, orc, case):
     # starts a new tile at row L - sq, so the tiles group rows differently)
     again = gqa.decode(q, kc, vc, sl)
     torch.cuda.synchronize()
-    assert (got - again).abs().max().item() <= 2e-5
+    assert (got - again).abs().max().item() <= REORDER_TOL
 
 
 def test_append_splits_and_merge_modes(gqa, orc):
@@ -138,7 +143,7 @@ def test_paged_matches_oracle_and_decode(gqa, orc, case):
         # a contiguous cache of more than 32 query rows per KV head runs on
         # 32-row tiles shared by a multi-wave workgroup, the paged kernel on
         # 16-row tiles: the same sums in another order
-        assert (got - ref).abs().max().item() <= 2e-5
+        assert (got - ref).abs().max().item() <= REORDER_TOL
 
 
 def test_paged_piece_longer_than_page_window(gqa, orc):

@@ -2,8 +2,11 @@
 oracle through the C ABI.  Tolerance as for bf16 inputs (2e-3 max abs):
 the codes convert to bf16 exactly and accumulation is fp32.  With
 power-of-two scales the dequantized cache is exactly a bf16 cache, and the
-fp8 call must agree with gqa_decode on it to fp32 rounding (the score
-product sums the head dim in a different order)."""
+fp8 call must agree with gqa_decode on it to within REORDER_TOL: the score
+product sums the head dim in a different order, and each weight p is
+carried as bf16 hi + lo (about 16 significant bits), so a last-bit change
+of a score moves a weight by up to ~2^-16 of itself and an output by
+~1e-5; 1e-4 bounds that with room, 20x under TOL."""
 import math
 
 import numpy as np
@@ -14,6 +17,7 @@ import gqa_inputs as gi
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
+REORDER_TOL = 1e-4
 
 
 @pytest.fixture(scope="module")
@@ -83,7 +87,7 @@ def test_fp8_with_power_of_two_scales_is_a_bf16_cache(gqa, orc):
     torch.cuda.synchronize()
     assert float(np.abs(got.double().cpu().numpy() - want).max()) <= TOL
     # same values; the score product sums the head dim in another order
-    assert (got - ref).abs().max().item() <= 2e-5
+    assert (got - ref).abs().max().item() <= REORDER_TOL
 
 
 def test_fp8_unit_scales_through_decode(gqa, orc):
