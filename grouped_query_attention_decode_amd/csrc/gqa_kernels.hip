@@ -2064,11 +2064,20 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
         const bool full = t0 + TR <= tb && t0 + TR - 1 <= pc.L - a.sq;
         float sc[8];
         float mx = -INFINITY;
+        if (full) {
+            // one uniform branch: every row of the tile is visible to every query row
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = t0 + 16 * (i >> 2) + 4 * kg + (i & 3);
-            sc[i] = (full || (t < tb && t <= last)) ? s4[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sc[i]);
+            for (int i = 0; i < 8; ++i) {
+                sc[i] = s4[i >> 2][i & 3] * a.scale_log2;
+                mx = fmaxf(mx, sc[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = t0 + 16 * (i >> 2) + 4 * kg + (i & 3);
+                sc[i] = (t < tb && t <= last) ? s4[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sc[i]);
+            }
         }
         mx = max_x32(max_x16(mx));
         const bool need = mx > m_run + kSlack;
