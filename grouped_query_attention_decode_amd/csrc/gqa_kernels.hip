@@ -2237,23 +2237,29 @@ decode_mfw(const Args a, const int R, const int n_rb)
     }
 }
 
-// Combine pass for a deferred plan: one wave per (segment, query row) of a
-// split segment merges the row's partials, in chunk order (the same
-// log2-sum-exp merge as the in-kernel one).  Lane l holds elements
-// 4 l .. 4 l + 3 of the row; KB pieces' loads are in flight together.
+// Combine pass for a deferred plan: one wave per (segment, RPW query rows)
+// of a split segment merges the rows' partials, in chunk order (the same
+// log2-sum-exp merge as the in-kernel one).  D / 4 lanes per row, lane l
+// holding elements 4 (l % (D / 4)) .. + 3 of row l / (D / 4); KB pieces'
+// loads are in flight together.
+template <int D>
+constexpr int combine_rows_per_wave() { return kWave / (D / 4); }
+
 template <int D, int RB>
 __global__ void __launch_bounds__(kWave)
 combine_rows(const Args a, const int R, const int n_rb, const int P)
 {
     constexpr int KB = 16;
+    constexpr int RPW = combine_rows_per_wave<D>();
+    static_assert(RB % RPW == 0, "rows of a block split evenly over the waves");
     const int lane = threadIdx.x & (kWave - 1);
-    const int r = blockIdx.x % RB;
-    const long long seg = blockIdx.x / RB;
+    const int r = (blockIdx.x % (RB / RPW)) * RPW + lane / (D / 4);
+    const long long seg = blockIdx.x / (RB / RPW);
     const int rb = (int)(seg % n_rb);
     const int g = (int)((seg / n_rb) % a.G);
     const int b = (int)(seg / ((long long)n_rb * a.G));
     const int row = rb * RB + r;
-    if (row >= R) return;
+    if (rb * RB + (r - r % RPW) >= R) return;   // every row of this wave is past R
     const int L = clamp_len(a.seq_lens, b, a.T);
     if (L == 0) return;
     // cost units before sequence b, and in total (every wave of the grid agrees)
@@ -2274,7 +2280,8 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
     const bool tail1 = cm.start(c_first) < off;
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
     const MSlots ms = mslots<D>(a);
-    const int e = 4 * min(lane, D / 4 - 1);
+    const int e = 4 * (lane % (D / 4));
+    const int rl = min(r, R - 1 - rb * RB);   // a lane past R reads the last live row (its result is dropped)
     float M = -INFINITY, den = 0.0f;
     float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int k0 = 0; k0 < npieces; k0 += KB) {
@@ -2283,8 +2290,8 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
         for (int kk = 0; kk < KB; ++kk) {
             const int k = min(k0 + kk, npieces - 1);
             const int base = ms.base(c_first + k, k == 0 && tail1 ? 1 : 0);
-            lse[kk] = load_coherent(part, base + ms.lse + r);
-            load4_coherent(part, base + r * D + e, ov[kk]);
+            lse[kk] = load_coherent(part, base + ms.lse + rl);
+            load4_coherent(part, base + rl * D + e, ov[kk]);
         }
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
@@ -2295,7 +2302,7 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
             for (int q = 0; q < 4; ++q) num[q] = fmaf(num[q], sc, w * ov[kk][q]);
         }
     }
-    if (lane < D / 4) {
+    if (row < R) {
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;
         const int64_t qrow = (int64_t)b * a.H * a.sq + (int64_t)g * R + row;
         *reinterpret_cast<float4*>(a.out + qrow * D + e) =
@@ -2416,8 +2423,9 @@ hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave * p.wg_waves), 0, stream, a, p.R, p.n_rb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !comb) return e;
-    const int64_t rows = (int64_t)a.B * a.G * p.n_rb * p.row_block;
-    hipLaunchKernelGGL(comb, dim3((unsigned)rows), dim3(kWave), 0, stream, a, p.R, p.n_rb, (int)p.grid);
+    const int rpw = p.D == 64 ? combine_rows_per_wave<64>() : combine_rows_per_wave<128>();
+    const int64_t waves = (int64_t)a.B * a.G * p.n_rb * (p.row_block / rpw);
+    hipLaunchKernelGGL(comb, dim3((unsigned)waves), dim3(kWave), 0, stream, a, p.R, p.n_rb, (int)p.grid);
     return hipGetLastError();
 }
 

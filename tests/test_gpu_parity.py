@@ -205,10 +205,13 @@ def test_split_invariance_and_determinism(gqa, orc, dt, path_name):
         assert torch.equal(again, outs[3])
 
 
-@pytest.mark.parametrize("H,G,sq,D", [(32, 8, 1, 128), (32, 1, 1, 128), (32, 1, 2, 64), (24, 1, 2, 128)])
+@pytest.mark.parametrize("H,G,sq,D", [(32, 8, 1, 128), (32, 1, 1, 128), (32, 1, 2, 64), (24, 1, 2, 128),
+                                      (3, 1, 11, 128), (12, 4, 1, 64)])
 def test_merge_modes_match_oracle(gqa, orc, H, G, sq, D):
     """The in-kernel merge and the combine kernel both give the oracle's
-    result at several splits, and each gives the same bits on a second call."""
+    result at several splits, and each gives the same bits on a second call.
+    R = 33 and R = 3 leave a combine wave (2 rows at D = 128, 4 at D = 64)
+    with rows past R."""
     x = gi.make_custom(4, H, G, D, 777, sq, dtype="bf16", seed=300 + H + G + sq,
                        seq_lens=[777, 3, 400, 129])
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
