@@ -1178,16 +1178,19 @@ decode_mqk(const Args a, const int R, const int n_rb)
 // ---------------------------------------------------------------------------
 // Matrix-core pass: both products on the MFMA units (bf16 inputs).
 //
-// Per 16-row tile of cache rows t and the (up to) 16 query rows r of a
-// segment:
-//   S^T[t][r]  = K[t][:] . Q[r][:]           v_mfma_f32_16x16x32_bf16, A = K, B = Q^T
-//   O^T[d][r] += V^T[d][t] . P^T[t][r]        v_mfma_f32_16x16x16_bf16, A = V^T, B = P^T
-// The score accumulator gives lane l the scores of query row l % 16 at cache
-// rows 4 (l / 16) + 0..3 of the tile, which is exactly the B operand the V
-// product wants: the softmax weights never move between lanes.  V^T is read
-// back from LDS (the tile is stored row-major; each lane gathers four rows of
-// one column).  Every output element of lane l belongs to query row l % 16,
-// so a rescale multiplies a lane's accumulators by one factor.
+// Per tile of cache rows t (32, as two 16-row halves h) and each block of
+// (up to) 16 query rows r of a segment:
+//   S^T_h[t][r] = K_h[t][:] . Q[r][:]         v_mfma_f32_16x16x32_bf16, A = K, B = Q^T
+//   O^T[d][r]  += V^T[d][t] . P^T[t][r]       v_mfma_f32_16x16x32_bf16, A = V^T, B = P^T
+// The score accumulator of half h gives lane l the scores of query row
+// l % 16 at cache rows 16 h + 4 (l / 16) + 0..3, and the V product takes
+// its k index 8 (l / 16) + i as tile row 16 (i / 4) + 4 (l / 16) + i % 4:
+// the weights are already where its B operand wants them and never move
+// between lanes.  V^T comes from the row-major LDS copy of the tile by the
+// transpose read below.  Every output element of lane l belongs to query
+// row l % 16, so a rescale multiplies a lane's accumulators by one factor.
+// (With 16-row tiles the V product is v_mfma_f32_16x16x16_bf16, k index
+// 4 (l / 16) + i as row 4 (l / 16) + i.)
 //
 // The weights p (fp32, in (0, 2^kSlack]) enter the V product as two bf16
 // terms, p = hi + lo, which keeps about 16 bits of each weight; V is exact in
