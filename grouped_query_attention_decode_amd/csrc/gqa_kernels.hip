@@ -1550,7 +1550,6 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     const int la = pc.L - a.sq;
     const int64_t nslab = ((int64_t)pc.b * a.G + pc.g) * a.sq * D;
     int wpage0 = 0;                      // paged: first page of the LDS window
-    bool wnew = false;                   // append: the window holds the new tokens' rows
     int tend = tb;                       // end of the current row window
     // paged: pages of the rows the next load_tile reads (the K rows of both
     // halves, the V rows), looked up one tile ahead so the LDS latency hides
@@ -1578,8 +1577,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             return static_cast<const char*>(base) + r * D * ES;
         } else if constexpr (SRC == kSrcAppend) {
             (void)pg;
-            return wnew ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * ES
-                        : static_cast<const char*>(base) + (slab + (int64_t)t * D) * ES;
+            return t >= la ? static_cast<const char*>(fresh) + (nslab + (int64_t)(t - la) * D) * ES
+                           : static_cast<const char*>(base) + (slab + (int64_t)t * D) * ES;
         } else {
             (void)fresh;
             (void)pg;
@@ -1649,7 +1648,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         }
         if constexpr (SRC == kSrcAppend) {
             // the first row block's pieces store the new tokens' rows into the cache
-            if (wnew && pc.rb == 0) {
+            if (pc.rb == 0 && t0 + TR > la) {
 #pragma unroll
                 for (int h = 0; h < NH; ++h) {
                     const int tk = t0 + 16 * h + col;
@@ -1762,9 +1761,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     // the window), so the compiler waits for exactly the oldest tile.  A
     // paged cache walks the piece in row windows whose pages fit the LDS
     // copy of the block table (one window unless the piece spans more than
-    // kPageWindow pages).
-    // An append walks the cache rows below L - sq, then the new tokens' rows,
-    // as two windows (so a window reads one source, chosen once).
+    // kPageWindow pages).  An append reads each row from the cache or, for
+    // the new tokens' rows, from k_new / v_new, in one window.
     for (int w0 = ta; w0 < tb; w0 = tend) {
         if constexpr (SRC == kSrcPaged) {
             wpage0 = w0 >> a.page_shift;
@@ -1774,9 +1772,6 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
             wave_lds_fence();            // the previous window's page reads are done
             for (int i = lane; i < np; i += kWave) sm.pages[i] = bt[i];
             wave_lds_fence();
-        } else if constexpr (SRC == kSrcAppend) {
-            wnew = w0 >= la;
-            tend = wnew ? tb : min(tb, la);
         }
         lookup(w0);
         constexpr int NBUF = mfa_buffers<NB, KV8>();

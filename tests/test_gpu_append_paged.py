@@ -6,8 +6,8 @@ Tolerances as for gqa_decode (bf16 inputs, fp32 accumulation: 2e-3 max
 abs).  The cache rows an append writes are compared bit for bit; a paged
 decode is also compared bit for bit with gqa_decode on the cache it
 describes where both run the same kernel on the same tiles, otherwise to
-within REORDER_TOL, as is an append (its tiles restart at the first new
-row).  REORDER_TOL: the same sums in another order -- each weight p is
+within REORDER_TOL, as is an append with gqa_decode on the appended cache.
+REORDER_TOL: the same sums in another order -- each weight p is
 carried as bf16 hi + lo (about 16 significant bits), so a change in the
 last bit of a score can move a weight by ~2^-16 of itself and an output by
 ~1e-5; 1e-4 bounds that with room, 20x under TOL."""
@@ -73,8 +73,7 @@ def test_append_matches_oracle_and_decode(gqa, orc, case):
     assert _err(got, want) <= TOL
     assert np.array_equal(kc.double().cpu().numpy(), k_after)
     assert np.array_equal(vc.double().cpu().numpy(), v_after)
-    # the same as gqa_decode on the appended cache, to rounding (the append
-    # starts a new tile at row L - sq, so the tiles group rows differently)
+    # the same as gqa_decode on the appended cache, to rounding
     again = gqa.decode(q, kc, vc, sl)
     torch.cuda.synchronize()
     assert (got - again).abs().max().item() <= REORDER_TOL
