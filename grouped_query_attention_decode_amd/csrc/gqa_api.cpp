@@ -117,8 +117,9 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     p->row_block = pow2_ceil(R < gqa::kMaxRowBlock ? R : gqa::kMaxRowBlock);
     if (p->path == gqa::Path::MFMA_QK && p->row_block < 4) p->row_block = 4;   // one k group of the 16x16 tile
     // matrix-core path: 16, 32 or 64 query rows (one to four 16-row MFMA
-    // blocks) share each K/V tile a wave reads
-    if (p->path == gqa::Path::MFMA) p->row_block = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+    // blocks) share each K/V tile a wave reads; a plain bf16 cache with more
+    // than 64 rows uses 128-row segments (eight waves of a workgroup)
+    if (p->path == gqa::Path::MFMA) p->row_block = R <= 16 ? 16 : R <= 32 ? 32 : (R <= 64 || src != 0 || fp8) ? 64 : 128;
     p->n_rb = (R + p->row_block - 1) / p->row_block;
     if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
         return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
@@ -135,9 +136,10 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
     // then one wave on each of the four SIMDs of a compute unit.  So does an
     // fp8 cache (half the bytes per tile for the same arithmetic).
-    // More than 32 query rows of a plain bf16 cache: workgroups of four
-    // waves sharing each K/V tile through LDS, two waves per SIMD (up to 32
-    // rows one wave carrying two blocks measured faster).
+    // More than 32 query rows of a plain bf16 cache: workgroups of four (64
+    // rows) or eight (128 rows) waves sharing each K/V tile through LDS, two
+    // waves per SIMD (up to 32 rows one wave carrying two blocks measured
+    // faster).
     p->wg_waves = (p->path == gqa::Path::MFMA && !p->kv_fp8 && src == 0 && p->row_block >= 64)
                       ? p->row_block / 16 : 1;
     int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;

@@ -1953,7 +1953,7 @@ decode_mfa(const Args a, const int R, const int n_rb)
 
 // ---------------------------------------------------------------------------
 // Matrix-core pass for groups of more than 32 query rows.  A workgroup of NW
-// waves (NW = 4) owns segments of 16 NW query rows; wave w computes rows
+// waves (NW = 4 or 8) owns segments of 16 NW query rows; wave w computes rows
 // 16 w .. 16 w + 15, and the NW waves share every K/V tile of 32 cache rows:
 // the workgroup loads it once (each thread a share of its 16-byte chunks,
 // one tile ahead in registers) and stages it in LDS, double-buffered, one
@@ -2353,6 +2353,7 @@ static DecodeFn pick(const Plan& p)
     if (p.path == Path::MFMA && p.wg_waves > 1) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
         if (p.wg_waves == 4) return p.D == 64 ? decode_mfw<64, 4> : decode_mfw<128, 4>;
+        if (p.wg_waves == 8) return p.D == 64 ? decode_mfw<64, 8> : decode_mfw<128, 8>;
         return nullptr;
     }
     if (p.path == Path::MFMA) {
@@ -2404,6 +2405,7 @@ static CombineFn pick_combine(const Plan& p)
     case 16: return p.D == 64 ? combine_rows<64, 16> : combine_rows<128, 16>;
     case 32: return p.D == 64 ? combine_rows<64, 32> : combine_rows<128, 32>;
     case 64: return p.D == 64 ? combine_rows<64, 64> : combine_rows<128, 64>;
+    case 128: return p.D == 64 ? combine_rows<64, 128> : combine_rows<128, 128>;
     default: return nullptr;
     }
 }

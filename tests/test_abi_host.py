@@ -93,15 +93,18 @@ def test_plan_row_blocks_for_large_groups(lib):
 
 
 def test_plan_matrix_path_row_blocks(lib):
-    """The matrix-core path packs 16, 32 or 64 query rows per segment, so the
-    K/V of a group is read once for up to 64 rows."""
+    """The matrix-core path packs 16, 32, 64 or (a plain bf16 cache) 128
+    query rows per segment, so the K/V of a group is read once for up to 128
+    rows."""
     cases = [  # (H, G, sq) -> rows, row block, row blocks
         ((32, 8, 1), 4, 16, 1),
         ((32, 4, 2), 16, 16, 1),
         ((32, 1, 1), 32, 32, 1),
         ((6, 1, 3), 18, 32, 1),
         ((32, 1, 2), 64, 64, 1),
-        ((32, 1, 3), 96, 64, 2),
+        ((32, 1, 3), 96, 128, 1),
+        ((32, 8, 64), 256, 128, 2),
+        ((32, 1, 5), 160, 128, 2),
     ]
     for (H, G, sq), rows, rb, nrb in cases:
         p = gqa.plan(_shape(H=H, G=G, sq=sq))

@@ -113,9 +113,9 @@ EDGE = [
     (2, 8, 4, 64, 50, 3, "bf16", [2, 3]),                # rows that see nothing
     (1, 4, 2, 128, 1, 1, "f32", None),                   # T = 1
     (2, 32, 1, 128, 300, 2, "bf16", [300, 123]),         # R=64: four 16-row blocks per wave
-    (2, 32, 1, 64, 200, 3, "bf16", [200, 50]),           # R=96: two 64-row segments, second half live
+    (2, 32, 1, 64, 200, 3, "bf16", [200, 50]),           # R=96: one 128-row segment, 96 rows live
     (2, 24, 1, 128, 150, 2, "bf16", [150, 149]),         # R=48: last 16-row block padding only
-    (2, 8, 2, 128, 300, 33, "bf16", [300, 40]),          # R=132: three 64-row segments
+    (2, 8, 2, 128, 300, 33, "bf16", [300, 40]),          # R=132: two 128-row segments, 4 rows live in the second
     (1, 32, 8, 64, 200, 64, "bf16", [200]),              # sq=64, R=256
     (1, 4, 1, 64, 100, 64, "bf16", [10]),                # sq > L: the first 54 new tokens see nothing
 ]
