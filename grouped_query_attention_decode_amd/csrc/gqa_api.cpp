@@ -132,7 +132,12 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     const int64_t min_share = 2 * (int64_t)gqa::cache_rows_per_wave_tile(*p);
     // One-wave workgroups: kWavesPerCU per compute unit (fewer if they do not
     // fit) -- enough loads in flight to saturate HBM; more waves only add
-    // pieces, and so partials and merges.
+    // pieces, and so partials and merges.  A matrix-core wave with one 16-row
+    // query block of a bf16 cache keeps two 32-row tiles (32 KB) in flight:
+    // two such waves per compute unit stream faster than three (batched
+    // GQA-8 decode 64.5 -> 63.5 us, the sq = 2 sweep at G = 32 / 4 4.5% / 2%
+    // faster, measured on two boxes), while two query blocks per wave (MQA)
+    // still want three.
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
     // then one wave on each of the four SIMDs of a compute unit.  So does an
     // fp8 cache (half the bytes per tile for the same arithmetic).
@@ -142,7 +147,9 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // faster).
     p->wg_waves = (p->path == gqa::Path::MFMA && !p->kv_fp8 && src == 0 && p->row_block >= 64)
                       ? p->row_block / 16 : 1;
-    int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4 : gqa::kWavesPerCU;
+    int want = (p->path == gqa::Path::MFMA && (p->row_block >= 64 || p->kv_fp8)) ? 4
+               : (p->path == gqa::Path::MFMA && p->row_block == 16) ? gqa::kWavesPerCUOneBlock
+                                                                      : gqa::kWavesPerCU;
     if (p->wg_waves > 1) want = gqa::kMultiWaveWavesPerCU / p->wg_waves;
     int occ = gqa::resident_groups_per_cu(*p);
     if (occ <= 0 || occ > want) occ = want;
