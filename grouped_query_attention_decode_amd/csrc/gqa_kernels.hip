@@ -2237,29 +2237,66 @@ decode_mfw(const Args a, const int R, const int n_rb)
     }
 }
 
-// Combine pass for a deferred plan: one wave per (segment, RPW query rows)
+// Combine pass for a deferred plan: one wave per (segment, RW query rows)
 // of a split segment merges the rows' partials, in chunk order (the same
-// log2-sum-exp merge as the in-kernel one).  D / 4 lanes per row, lane l
-// holding elements 4 (l % (D / 4)) .. + 3 of row l / (D / 4); KB pieces'
-// loads are in flight together.
+// log2-sum-exp merge as the in-kernel one).  D / 4 lanes per row: a lane
+// holds elements 4 (l % (D / 4)) .. + 3 of row l / (D / 4) of each of the
+// wave's NG groups of RPW rows.  With few pieces per segment (NG = 2 or 4)
+// one schedule walk serves RW = RPW * NG rows and the loads of several rows'
+// pieces are in flight together; with many (NG = 1) each wave keeps up to 16
+// pieces of its RPW rows in flight.
 template <int D>
-constexpr int combine_rows_per_wave() { return kWave / (D / 4); }
+constexpr int combine_rows_per_group() { return kWave / (D / 4); }
 
-template <int D, int RB>
+// Merge the pieces of row groups G0 .. G0 + NG - 1 (row rl[g] of the slots),
+// KB pieces' loads in flight per group at a time.  Pieces past the last are
+// clamped to it and weighted 0, so the per-row arithmetic does not depend on
+// KB or on the grouping.
+template <int D, int KB, int G0, int NG>
+__device__ __forceinline__ void combine_groups(__amdgpu_buffer_rsrc_t part, const MSlots& ms, int c_first,
+                                               int npieces, bool tail1, const int* rl, int e, float* M, float* den,
+                                               float (*num)[4])
+{
+    for (int k0 = 0; k0 < npieces; k0 += KB) {
+        float lse[NG][KB], ov[NG][KB][4];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int k = min(k0 + kk, npieces - 1);
+            const int base = ms.base(c_first + k, k == 0 && tail1 ? 1 : 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                lse[g][kk] = load_coherent(part, base + ms.lse + rl[G0 + g]);
+                load4_coherent(part, base + rl[G0 + g] * D + e, ov[g][kk]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                float w;
+                const float sc = lse_step(M[G0 + g], k0 + kk < npieces ? lse[g][kk] : -INFINITY, &w);
+                den[G0 + g] = fmaf(den[G0 + g], sc, w);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) num[G0 + g][q] = fmaf(num[G0 + g][q], sc, w * ov[g][kk][q]);
+            }
+    }
+}
+
+template <int D, int RB, int NG>
 __global__ void __launch_bounds__(kWave)
 combine_rows(const Args a, const int R, const int n_rb, const int P)
 {
-    constexpr int KB = 16;
-    constexpr int RPW = combine_rows_per_wave<D>();
-    static_assert(RB % RPW == 0, "rows of a block split evenly over the waves");
+    constexpr int RPW = combine_rows_per_group<D>();
+    constexpr int RW = RPW * NG;
+    static_assert(RB % RW == 0, "rows of a block split evenly over the waves");
+    static_assert(NG == 1 || NG == 2 || NG == 4, "groups per wave");
     const int lane = threadIdx.x & (kWave - 1);
-    const int r = (blockIdx.x % (RB / RPW)) * RPW + lane / (D / 4);
-    const long long seg = blockIdx.x / (RB / RPW);
+    const int rw0 = (int)(blockIdx.x % (RB / RW)) * RW;   // first row of this wave within the segment
+    const long long seg = blockIdx.x / (RB / RW);
     const int rb = (int)(seg % n_rb);
     const int g = (int)((seg / n_rb) % a.G);
     const int b = (int)(seg / ((long long)n_rb * a.G));
-    const int row = rb * RB + r;
-    if (rb * RB + (r - r % RPW) >= R) return;   // every row of this wave is past R
+    if (rb * RB + rw0 >= R) return;            // every row of this wave is past R
     const int L = clamp_len(a.seq_lens, b, a.T);
     if (L == 0) return;
     // cost units before sequence b, and in total (every wave of the grid agrees)
@@ -2281,32 +2318,44 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
     const MSlots ms = mslots<D>(a);
     const int e = 4 * (lane % (D / 4));
-    const int rl = min(r, R - 1 - rb * RB);   // a lane past R reads the last live row (its result is dropped)
-    float M = -INFINITY, den = 0.0f;
-    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < npieces; k0 += KB) {
-        float lse[KB], ov[KB][4];
+    int rl[NG];
+    float M[NG], den[NG], num[NG][4];
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-            const int k = min(k0 + kk, npieces - 1);
-            const int base = ms.base(c_first + k, k == 0 && tail1 ? 1 : 0);
-            lse[kk] = load_coherent(part, base + ms.lse + rl);
-            load4_coherent(part, base + rl * D + e, ov[kk]);
+    for (int gi = 0; gi < NG; ++gi) {
+        const int r = rw0 + gi * RPW + lane / (D / 4);
+        rl[gi] = min(r, R - 1 - rb * RB);      // a lane past R reads the last live row (its result is dropped)
+        M[gi] = -INFINITY;
+        den[gi] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) num[gi][q] = 0.0f;
+    }
+    // at most 16 (group, piece) loads in flight; the batch fits the piece count
+    if (npieces <= 4) {
+        combine_groups<D, 4, 0, NG>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+    } else if (npieces <= 8) {
+        if constexpr (NG == 1) {
+            combine_groups<D, 8, 0, 1>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+        } else {
+            combine_groups<D, 8, 0, NG / 2>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+            combine_groups<D, 8, NG / 2, NG / 2>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
         }
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-            float w;
-            const float sc = lse_step(M, k0 + kk < npieces ? lse[kk] : -INFINITY, &w);
-            den = fmaf(den, sc, w);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) num[q] = fmaf(num[q], sc, w * ov[kk][q]);
+    } else {
+        combine_groups<D, 16, 0, 1>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+        if constexpr (NG >= 2) combine_groups<D, 16, 1, 1>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+        if constexpr (NG >= 4) {
+            combine_groups<D, 16, 2, 1>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
+            combine_groups<D, 16, 3, 1>(part, ms, c_first, npieces, tail1, rl, e, M, den, num);
         }
     }
-    if (row < R) {
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        const int64_t qrow = (int64_t)b * a.H * a.sq + (int64_t)g * R + row;
-        *reinterpret_cast<float4*>(a.out + qrow * D + e) =
-            make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int row = rw0 + gi * RPW + lane / (D / 4);
+        if (rb * RB + row < R) {
+            const float inv = den[gi] > 0.0f ? 1.0f / den[gi] : 0.0f;
+            const int64_t qrow = (int64_t)b * a.H * a.sq + (int64_t)g * R + rb * RB + row;
+            *reinterpret_cast<float4*>(a.out + qrow * D + e) =
+                make_float4(num[gi][0] * inv, num[gi][1] * inv, num[gi][2] * inv, num[gi][3] * inv);
+        }
     }
 }
 
@@ -2400,14 +2449,42 @@ int cache_rows_per_wave_tile(const Plan& p)
 
 typedef void (*CombineFn)(const Args, int, int, int);
 
-static CombineFn pick_combine(const Plan& p)
+template <int NG>
+static CombineFn pick_combine_ng(const Plan& p)
+{
+    switch (p.row_block) {
+    case 16: return p.D == 64 ? combine_rows<64, 16, NG> : combine_rows<128, 16, NG>;
+    case 32: return p.D == 64 ? combine_rows<64, 32, NG> : combine_rows<128, 32, NG>;
+    case 64: return p.D == 64 ? combine_rows<64, 64, NG> : combine_rows<128, 64, NG>;
+    case 128: return p.D == 64 ? combine_rows<64, 128, NG> : combine_rows<128, 128, NG>;
+    default: return nullptr;
+    }
+}
+
+// Row groups per combine wave from the expected pieces per segment (the
+// planner's estimate: workgroups per segment, plus the two partial ends):
+// up to 4 pieces, four groups share one schedule walk and one load batch;
+// up to 8, two; more, one group per wave with 16 pieces in flight
+// (measured: multi-token ~4 pieces 78.6 -> 73.8 us per step; MQA ~14 and the
+// sq = 2 sweep at G = 1 ~34 pieces lose 3-5 us with four groups).
+static int combine_groups_for(const Plan& p, const Args& a)
+{
+    const int64_t segs = (int64_t)a.B * a.G * p.n_rb;
+    const int64_t pieces = segs > 0 ? p.grid / segs + 2 : 1;
+    int ng = pieces <= 4 ? 4 : pieces <= 8 ? 2 : 1;
+    while (ng > 1 && p.row_block % (combine_rows_per_group<128>() * ng) != 0) ng /= 2;
+    if (p.D == 64)
+        while (ng > 1 && p.row_block % (combine_rows_per_group<64>() * ng) != 0) ng /= 2;
+    return ng;
+}
+
+static CombineFn pick_combine(const Plan& p, int ng)
 {
     if (p.path != Path::MFMA) return nullptr;
-    switch (p.row_block) {
-    case 16: return p.D == 64 ? combine_rows<64, 16> : combine_rows<128, 16>;
-    case 32: return p.D == 64 ? combine_rows<64, 32> : combine_rows<128, 32>;
-    case 64: return p.D == 64 ? combine_rows<64, 64> : combine_rows<128, 64>;
-    case 128: return p.D == 64 ? combine_rows<64, 128> : combine_rows<128, 128>;
+    switch (ng) {
+    case 1: return pick_combine_ng<1>(p);
+    case 2: return pick_combine_ng<2>(p);
+    case 4: return pick_combine_ng<4>(p);
     default: return nullptr;
     }
 }
@@ -2418,14 +2495,15 @@ hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
     DecodeFn fn = pick(p);
     if (!fn) return hipErrorInvalidValue;
     CombineFn comb = nullptr;
+    const int ng = combine_groups_for(p, a);
     if (p.deferred) {
-        comb = pick_combine(p);
+        comb = pick_combine(p, ng);
         if (!comb || a.deferred != 1) return hipErrorInvalidValue;
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave * p.wg_waves), 0, stream, a, p.R, p.n_rb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !comb) return e;
-    const int rpw = p.D == 64 ? combine_rows_per_wave<64>() : combine_rows_per_wave<128>();
+    const int rpw = (p.D == 64 ? combine_rows_per_group<64>() : combine_rows_per_group<128>()) * ng;
     const int64_t waves = (int64_t)a.B * a.G * p.n_rb * (p.row_block / rpw);
     hipLaunchKernelGGL(comb, dim3((unsigned)waves), dim3(kWave), 0, stream, a, p.R, p.n_rb, (int)p.grid);
     return hipGetLastError();
