@@ -1890,6 +1890,23 @@ __device__ __forceinline__ void merge_pieces(const Args& a, const Pending& pd, i
     }
 }
 
+// merge_pieces with its load batch cut to the piece count: a segment split in
+// 2-4 pieces (the common case when the workgroups outnumber the segments a
+// few times) loads 4 pieces per batch instead of re-loading its last piece up
+// to 16 times (the merge on the step's critical path: batched GQA-8
+// 63.6 -> 62.8 us, fp8 40.9 -> 39.8, append 64.3 -> 63.2).
+template <int D, int NF, int KBMAX>
+__device__ __forceinline__ void merge_pieces_n(const Args& a, const Pending& pd, int lane, int r0, int rows,
+                                               const ChunkMap& cm)
+{
+    if (pd.npieces <= 4)
+        merge_pieces<D, NF, (KBMAX < 4 ? KBMAX : 4)>(a, pd, lane, r0, rows, cm);
+    else if (pd.npieces <= 8)
+        merge_pieces<D, NF, (KBMAX < 8 ? KBMAX : 8)>(a, pd, lane, r0, rows, cm);
+    else
+        merge_pieces<D, NF, KBMAX>(a, pd, lane, r0, rows, cm);
+}
+
 // Count this wave's arrival for a pending segment of RB rows; the last
 // arrival merges, 16 rows at a time (choosing the lane layout by the number
 // of live rows), and resets the counter.  The caller has waited for its own
@@ -1909,13 +1926,13 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
         // lanes per row: 64 / (rows rounded up to a power of two), at most D / 4;
         // about 32 to 48 loads of a batch in flight per lane
         if (rows > 8)
-            merge_pieces<D, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, cm);
+            merge_pieces_n<D, D / 16, (D == 128 ? 4 : 8)>(a, pd, lane, r0, rows, cm);
         else if (rows > 4)
-            merge_pieces<D, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, cm);
+            merge_pieces_n<D, D / 32, (D == 128 ? 8 : 16)>(a, pd, lane, r0, rows, cm);
         else if (rows > 2 || D == 64)
-            merge_pieces<D, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, cm);
+            merge_pieces_n<D, (D == 128 ? 2 : 1), 16>(a, pd, lane, r0, rows, cm);
         else
-            merge_pieces<D, 1, 16>(a, pd, lane, r0, rows, cm);
+            merge_pieces_n<D, 1, 16>(a, pd, lane, r0, rows, cm);
     }
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
