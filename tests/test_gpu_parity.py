@@ -298,3 +298,77 @@ def test_both_paths_match_oracle(gqa, orc, path_name, G, sq):
     _compare(got, want, TOL["bf16"], "%s G=%d sq=%d" % (path_name, G, sq))
     p = gqa.plan(gqa.shape_of(x["q"], x["k"]), path=path)
     assert p["path"] == path
+
+
+def _pieces_per_segment(lens, G, n_rb, P, piece_cost=64):
+    """Pieces of each (sequence, KV head, row block) segment under the
+    matrix-core work split: segment costs L + piece_cost units (L > 0), all
+    end to end, cut into P equal chunks.  Host-side schedule arithmetic only,
+    used to check which merge branches a case reaches."""
+    costs = [(L + piece_cost) if L > 0 else 0 for L in lens]
+    units = G * n_rb
+    V = sum(costs) * units
+    P = min(P, V)
+
+    def chunk_of(x):
+        return ((x + 1) * P - 1) // V
+
+    out, before = [], 0
+    for L, c in zip(lens, costs):
+        for k in range(units if L > 0 else 0):
+            off = before * units + k * c + piece_cost
+            out.append(chunk_of(off + L - 1) - chunk_of(off) + 1)
+        before += c
+    return out
+
+
+def _combine_groups(segs, P, row_block, D):
+    """Row groups per combine wave the launcher picks: the expected pieces
+    per segment (workgroups per segment + 2) up to 4 -> 4, up to 8 -> 2,
+    else 1; fewer if the segment's rows do not split evenly."""
+    est = P // segs + 2
+    ng = 4 if est <= 4 else 2 if est <= 8 else 1
+    rpg = 64 // (D // 4)
+    while ng > 1 and row_block % (rpg * ng) != 0:
+        ng //= 2
+    return ng
+
+
+# (B, H, G, D, T, sq, seq_lens, workgroups, row groups, piece-count branches reached)
+_COMBINE_CASES = [
+    (8, 32, 8, 128, 1024, 1, None, 128, 4, {"<=4"}),
+    (8, 4, 1, 128, 4096, 1, [4096] + [16] * 7, 16, 4, {">8"}),
+    (8, 4, 1, 128, 4096, 1, [4096] + [16] * 7, 40, 2, {">8"}),
+    (8, 4, 1, 128, 4096, 1, [4096] + [16] * 7, 100, 1, {"<=4", ">8"}),
+    (4, 4, 1, 64, 2048, 1, [2048, 700, 64, 1], 24, 2, {"<=4", "5-8", ">8"}),
+    (4, 32, 1, 128, 2048, 1, [2048, 1500, 900, 33], 8, 4, {"<=4"}),
+    (4, 32, 1, 128, 2048, 1, [2048, 1500, 900, 33], 20, 2, {"5-8"}),
+    (2, 32, 8, 128, 512, 64, [512, 300], 64, 4, {"<=4"}),
+]
+
+
+@pytest.mark.parametrize("case", _COMBINE_CASES, ids=lambda c: "B%d_H%d_G%d_D%d_sq%d_P%d" % (c[0], c[1], c[2], c[3], c[5], c[7]))
+def test_combine_row_groups_match_in_kernel_merge(gqa, orc, case):
+    """The combine kernel with one, two or four row groups per wave, over
+    segments of up to 4, 5-8 and more than 8 pieces: oracle parity, and the
+    same bits as the in-kernel merge of the same split (both merge a row's
+    pieces in chunk order with the same arithmetic; padding pieces carry
+    weight 0)."""
+    B, H, G, D, T, sq, lens, P, ng_want, branches = case
+    R = H // G * sq
+    row_block = 16 if R <= 16 else 32 if R <= 32 else 64 if R <= 64 else 128
+    n_rb = -(-R // row_block)
+    lens_eff = lens if lens is not None else [T] * B
+    segs = B * G * n_rb
+    assert _combine_groups(segs, P, row_block, D) == ng_want
+    pieces = [n for n in _pieces_per_segment(lens_eff, G, n_rb, P) if n > 1]
+    got_branches = {("<=4" if n <= 4 else "5-8" if n <= 8 else ">8") for n in pieces}
+    assert branches <= got_branches, (branches, got_branches)
+
+    x = gi.make_custom(B, H, G, D, T, sq, dtype="bf16", seed=900 + P + D, seq_lens=lens)
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
+    xc = _to(x, "cuda")
+    comb = _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=gqa.MERGE_COMBINE)
+    _compare(comb, want, TOL["bf16"], "combine P=%d" % P)
+    ink = _run(gqa, xc, path=gqa.PATH_MFMA, workgroups=P, merge=gqa.MERGE_IN_KERNEL)
+    assert torch.equal(comb, ink), "combine and in-kernel merge differ: %g" % (comb - ink).abs().max().item()
