@@ -2488,10 +2488,9 @@ static int combine_groups_for(const Plan& p, const Args& a)
 {
     const int64_t segs = (int64_t)a.B * a.G * p.n_rb;
     const int64_t pieces = segs > 0 ? p.grid / segs + 2 : 1;
+    const int rpg = p.D == 64 ? combine_rows_per_group<64>() : combine_rows_per_group<128>();
     int ng = pieces <= 4 ? 4 : pieces <= 8 ? 2 : 1;
-    while (ng > 1 && p.row_block % (combine_rows_per_group<128>() * ng) != 0) ng /= 2;
-    if (p.D == 64)
-        while (ng > 1 && p.row_block % (combine_rows_per_group<64>() * ng) != 0) ng /= 2;
+    while (ng > 1 && p.row_block % (rpg * ng) != 0) ng /= 2;   // a wave's rows within one segment
     return ng;
 }
 
