@@ -265,36 +265,28 @@ def main(argv=None):
     iso_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
 
     # (2) The timed region: K steps back to back, each after the cache sweep,
-    #     bracketed by synchronize on both sides, with an event before each
-    #     sweep and after each step; then the same K sweeps alone, with an
-    #     event around each.  Launches queue behind the sweeps, so dispatch
-    #     latency is hidden as in a decode loop.  Time per step = (total of
-    #     the K steps with their sweeps - total of the K sweeps) / K: the
-    #     kernels' device time plus the gap after the sweep kernel, averaged
-    #     over the whole timed region.  The median per step (median of
-    #     sweep + step minus median of sweep) is reported beside it.
-    pa = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    pb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    #     bracketed by synchronize on both sides; minus the same K sweeps
+    #     alone.  Launches queue behind the sweeps, so dispatch latency is
+    #     hidden as in a decode loop and the difference is the kernels'
+    #     device time -- what rocprofv3 reports per launch.
+    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    e0.record(stream)
     for i in range(K):
-        pa[i][0].record(stream)
         if not args.no_flush:
             flush.sum()
         call()
-        pa[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    e2.record(stream)
     for i in range(K):
-        pb[i][0].record(stream)
         if not args.no_flush:
             flush.sum()
-        pb[i][1].record(stream)
+    e3.record(stream)
     torch.cuda.synchronize()
-    with_step = [pa[i][0].elapsed_time(pa[i][1]) for i in range(K)]
-    sweep_only = [pb[i][0].elapsed_time(pb[i][1]) for i in range(K)]
-    ms = (pa[0][0].elapsed_time(pa[-1][1]) - pb[0][0].elapsed_time(pb[-1][1])) / K
-    ms_median = statistics.median(with_step) - statistics.median(sweep_only)
+    ms = (e0.elapsed_time(e1) - e2.elapsed_time(e3)) / K
     step_ms = iso_ms
     q = statistics.quantiles(step_ms, n=10) if K >= 10 else [min(step_ms)] * 9
 
@@ -337,7 +329,6 @@ def main(argv=None):
         },
         "us_per_step": round(ms * 1e3, 2),
         "timing": "device time per step: K steps back to back after cache sweeps, minus the sweeps alone",
-        "us_per_step_median": round(ms_median * 1e3, 2),
         "isolated_call_us_p10": round(q[0] * 1e3, 2),
         "isolated_call_us_p50": round(statistics.median(step_ms) * 1e3, 2),
         "isolated_call_us_p90": round(q[8] * 1e3, 2),
