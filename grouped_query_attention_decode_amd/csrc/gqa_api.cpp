@@ -136,7 +136,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // query block of a bf16 cache keeps two 32-row tiles (32 KB) in flight:
     // two such waves per compute unit stream faster than three (batched
     // GQA-8 decode 64.5 -> 63.5 us, the sq = 2 sweep at G = 32 / 4 4.5% / 2%
-    // faster, measured on two boxes), while two query blocks per wave (MQA)
+    // faster, measured on two machines), while two query blocks per wave (MQA)
     // still want three.
     // Four 16-row blocks per wave make the matrix-core kernel compute-bound:
     // then one wave on each of the four SIMDs of a compute unit.  So does an
