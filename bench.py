@@ -337,6 +337,12 @@ def main(argv=None):
         "flops": flops(w.H, w.D, w.sq, sum_len),
         "warm_cache_us_per_step": round(statistics.median(warm) * 1e3, 2),
         "wall_ms_per_step_incl_sweep": round(wall / K * 1e3, 4),
+        # the cache sweeps timed alone are a measured read-bandwidth probe: a
+        # 1 GiB fp32 sum (torch's reduction kernel) per sweep
+        "read_probe": (None if args.no_flush else {
+            "bytes": FLUSH_BYTES, "us": round(e2.elapsed_time(e3) / K * 1e3, 2),
+            "gbs": round(FLUSH_BYTES / (e2.elapsed_time(e3) / K * 1e-3) / 1e9, 1),
+            "kernel": "torch sum over a 1 GiB fp32 tensor"}),
         "max_abs_err_vs_oracle_b0": None,
         "roofline": {
             "bound": "hbm",
