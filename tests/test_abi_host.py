@@ -73,6 +73,25 @@ def test_plan_of_batched_gqa8(lib):
     assert q["workspace_bytes"] == (1 << 20) + _round256(q["workgroups"] * 2 * (4 * 128 + 16) * 4)
 
 
+def test_plan_grid_per_compute_unit(lib):
+    """One persistent workgroup grid per plan, sized per compute unit (256
+    on MI355X, and the planner's count when no device is visible): two
+    one-wave workgroups per CU when a wave carries one 16-row block of a bf16
+    cache, three with two blocks (MQA), four for an fp8 cache; multi-wave
+    workgroups (more than 32 rows per KV head) two waves per SIMD; small
+    caches capped by the pieces-per-segment bound."""
+    cu = 256
+    assert gqa.plan(_shape(B=32))["workgroups"] == 2 * cu                      # batched GQA-8
+    assert gqa.plan(_shape(B=16, G=32, sq=2, T=16384))["workgroups"] == 2 * cu  # MHA, 2 rows
+    assert gqa.plan(_shape(B=64, G=1, T=8192))["workgroups"] == 3 * cu         # MQA, 32 rows
+    fp8 = _shape(B=32, kv_dtype=gqa.GQA_FP8_E4M3)
+    assert gqa.plan(fp8)["workgroups"] == 4 * cu
+    assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == 2 * cu  # 64 rows: 4-wave groups
+    assert gqa.plan(_shape(B=8, G=8, sq=64))["workgroups"] == cu               # 256 rows: 8-wave groups
+    # one sequence of 8 KV heads: at most 32 pieces per segment
+    assert gqa.plan(_shape(B=1, G=8, D=64))["workgroups"] == 8 * 32
+
+
 def test_plan_workgroup_option(lib):
     p = gqa.plan(_shape(), workgroups=100)
     assert p["workgroups"] == 100
