@@ -264,29 +264,39 @@ def main(argv=None):
     torch.cuda.synchronize()
     iso_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
 
-    # (2) The timed region: K steps back to back, each after the cache sweep,
-    #     bracketed by synchronize on both sides; minus the same K sweeps
-    #     alone.  Launches queue behind the sweeps, so dispatch latency is
-    #     hidden as in a decode loop and the difference is the kernels'
-    #     device time -- what rocprofv3 reports per launch.
-    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    # (2) The timed region, bracketed by synchronize on both sides: K steps
+    #     back to back, each after the cache sweep, in blocks that alternate
+    #     with blocks of the same number of sweeps alone; per step, the
+    #     difference of the two totals.  Launches queue behind the sweeps, so
+    #     dispatch latency is hidden as in a decode loop and the difference is
+    #     the kernels' device time -- what rocprofv3 reports per launch.
+    #     Alternating short blocks cancels slow drift of the sweep's own speed
+    #     (clocks, power), which two long loops one after the other do not.
+    nblk = min(K, 10)
+    sizes = [K // nblk + (1 if b < K % nblk else 0) for b in range(nblk)]
+    ev_run = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nblk)]
+    ev_swp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nblk)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        if not args.no_flush:
-            flush.sum()
-        call()
-    e1.record(stream)
+    for b in range(nblk):
+        ev_run[b][0].record(stream)
+        for i in range(sizes[b]):
+            if not args.no_flush:
+                flush.sum()
+            call()
+        ev_run[b][1].record(stream)
+        ev_swp[b][0].record(stream)
+        for i in range(sizes[b]):
+            if not args.no_flush:
+                flush.sum()
+        ev_swp[b][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    e2.record(stream)
-    for i in range(K):
-        if not args.no_flush:
-            flush.sum()
-    e3.record(stream)
-    torch.cuda.synchronize()
-    ms = (e0.elapsed_time(e1) - e2.elapsed_time(e3)) / K
+    run_ms = sum(e[0].elapsed_time(e[1]) for e in ev_run)
+    swp_ms = sum(e[0].elapsed_time(e[1]) for e in ev_swp)
+    ms = (run_ms - swp_ms) / K
+    blk_us = sorted((ev_run[b][0].elapsed_time(ev_run[b][1]) - ev_swp[b][0].elapsed_time(ev_swp[b][1]))
+                    / sizes[b] * 1e3 for b in range(nblk))
     step_ms = iso_ms
     q = statistics.quantiles(step_ms, n=10) if K >= 10 else [min(step_ms)] * 9
 
@@ -328,7 +338,8 @@ def main(argv=None):
             "mode": args.mode,
         },
         "us_per_step": round(ms * 1e3, 2),
-        "timing": "device time per step: K steps back to back after cache sweeps, minus the sweeps alone",
+        "timing": "device time per step: K steps back to back after cache sweeps, minus as many sweeps alone, in %d alternating blocks" % nblk,
+        "block_us_min_max": [round(blk_us[0], 2), round(blk_us[-1], 2)],
         "isolated_call_us_p10": round(q[0] * 1e3, 2),
         "isolated_call_us_p50": round(statistics.median(step_ms) * 1e3, 2),
         "isolated_call_us_p90": round(q[8] * 1e3, 2),
@@ -336,12 +347,12 @@ def main(argv=None):
         "useful_bytes": ub,
         "flops": flops(w.H, w.D, w.sq, sum_len),
         "warm_cache_us_per_step": round(statistics.median(warm) * 1e3, 2),
-        "wall_ms_per_step_incl_sweep": round(wall / K * 1e3, 4),
+        "wall_ms_per_step_incl_two_sweeps": round(wall / K * 1e3, 4),
         # the cache sweeps timed alone are a measured read-bandwidth probe: a
         # 1 GiB fp32 sum (torch's reduction kernel) per sweep
         "read_probe": (None if args.no_flush else {
-            "bytes": FLUSH_BYTES, "us": round(e2.elapsed_time(e3) / K * 1e3, 2),
-            "gbs": round(FLUSH_BYTES / (e2.elapsed_time(e3) / K * 1e-3) / 1e9, 1),
+            "bytes": FLUSH_BYTES, "us": round(swp_ms / K * 1e3, 2),
+            "gbs": round(FLUSH_BYTES / (swp_ms / K * 1e-3) / 1e9, 1),
             "kernel": "torch sum over a 1 GiB fp32 tensor"}),
         "max_abs_err_vs_oracle_b0": None,
         "roofline": {
