@@ -79,7 +79,8 @@ def test_plan_grid_per_compute_unit(lib):
     one-wave workgroups per CU when a wave carries one 16-row block of a bf16
     cache, three with two blocks (MQA), four for an fp8 cache; multi-wave
     workgroups (more than 32 rows per KV head) two waves per SIMD; small
-    caches capped by the pieces-per-segment bound."""
+    caches: at least 256 cache rows per one-block bf16 wave, and at most 32
+    pieces per segment."""
     cu = 256
     assert gqa.plan(_shape(B=32))["workgroups"] == 2 * cu                      # batched GQA-8
     assert gqa.plan(_shape(B=16, G=32, sq=2, T=16384))["workgroups"] == 2 * cu  # MHA, 2 rows
@@ -88,17 +89,25 @@ def test_plan_grid_per_compute_unit(lib):
     assert gqa.plan(fp8)["workgroups"] == 4 * cu
     assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == 2 * cu  # 64 rows: 4-wave groups
     assert gqa.plan(_shape(B=8, G=8, sq=64))["workgroups"] == cu               # 256 rows: 8-wave groups
-    # one sequence of 8 KV heads: at most 32 pieces per segment
-    assert gqa.plan(_shape(B=1, G=8, D=64))["workgroups"] == 8 * 32
+    # small caches: at least 256 cache rows per one-block wave, then at most
+    # 32 pieces per segment
+    ex = gqa.plan(_shape(B=1, G=8, D=64))                                       # 8 x 4096 rows
+    assert ex["workgroups"] == 8 * 4096 // 256 and ex["combine"] == 0
+    assert gqa.plan(_shape(B=2, G=8, D=64))["workgroups"] == 2 * 8 * 4096 // 256
+    d128 = gqa.plan(_shape(B=1, G=8, D=128))
+    assert d128["workgroups"] == 8 * 4096 // 256 and d128["combine"] == 0       # 18 pieces x 2 KB merged in-kernel
+    assert gqa.plan(_shape(B=1, G=8, D=64, T=16384))["workgroups"] == 8 * 32    # pieces-per-segment bound
+    # the minimum applies to one-block bf16 waves only
+    assert gqa.plan(_shape(B=1, G=8, D=64, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 32
 
 
 def test_plan_workgroup_option(lib):
     p = gqa.plan(_shape(), workgroups=100)
     assert p["workgroups"] == 100
     small = gqa.plan(_shape(B=1, T=100))
-    # a tiny cache gets no more workgroups than it has pairs of wave tiles:
-    # 8 KV heads x 100 rows / (2 x 16 rows)
-    assert 1 <= small["workgroups"] <= 25
+    # a tiny cache gets no more workgroups than it has shares of 256 rows:
+    # 8 KV heads x 100 rows / 256
+    assert small["workgroups"] == 4
 
 
 def test_plan_row_blocks_for_large_groups(lib):
