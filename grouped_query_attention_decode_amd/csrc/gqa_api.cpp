@@ -130,14 +130,16 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // cache is so small that a share would drop below two tiles.
     const int64_t max_units = (int64_t)s->B * s->G * p->n_rb * s->T;
     int64_t min_share = 2 * (int64_t)gqa::cache_rows_per_wave_tile(*p);
-    // A matrix-core wave with one 16-row block of a bf16 cache pays a fixed
-    // cost per piece (its start, the partial, the merge) worth about 64
-    // streamed rows, so on small caches fewer, longer waves win: from 8 to
-    // 32 MB of K/V, waves of 170-340 rows were fastest (B = 1, D = 128,
-    // T = 4096: 512 waves and the combine kernel 24.2 us -> 128 waves 21.2 us;
-    // B = 2, D = 64: 512 -> 256 waves 21.0 -> 18.9 us; B = 1, D = 64:
-    // 256 -> 128 waves 14.0 -> 13.4 us by kernel trace).
-    if (p->path == gqa::Path::MFMA && p->row_block == 16 && !p->kv_fp8)
+    // A matrix-core wave with one 16-row query block pays a fixed cost per
+    // piece (its start, the partial, the merge) worth about 64 streamed rows,
+    // so on small caches fewer, longer waves win: from 8 to 32 MB of bf16
+    // K/V, waves of 170-340 rows were fastest (B = 1, D = 128, T = 4096: 512
+    // waves and the combine kernel 24.2 us -> 128 waves 21.2 us; B = 2,
+    // D = 64: 512 -> 256 waves 21.0 -> 18.9 us; B = 1, D = 64: 256 -> 128
+    // waves 14.0 -> 13.4 us by kernel trace); an fp8 cache likewise (B = 1,
+    // D = 128: 512 waves 22.8 us, 128 waves 20.2 us; D = 64: 18.0 -> 17.7 us);
+    // appended tokens and the paged cache were flat from 128 to 256 waves.
+    if (p->path == gqa::Path::MFMA && p->row_block == 16)
         min_share = std::max<int64_t>(min_share, gqa::kMinRowsPerWaveOneBlock);
     // One-wave workgroups: kWavesPerCU per compute unit (fewer if they do not
     // fit) -- enough loads in flight to saturate HBM; more waves only add

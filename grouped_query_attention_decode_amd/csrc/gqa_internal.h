@@ -14,7 +14,7 @@ constexpr int kMaxRowBlock = 16;   // query rows per VALU segment
 constexpr int kMaxSegments = 1 << 18;  // (sequence, KV head, row block) triples per call
 constexpr int kWavesPerCU = 3;     // one-wave workgroups per compute unit (measured best)
 constexpr int kWavesPerCUOneBlock = 2;  // matrix-core waves carrying one 16-row block of a bf16 cache
-constexpr int kMinRowsPerWaveOneBlock = 256;  // least cache rows per such wave on small caches (measured)
+constexpr int kMinRowsPerWaveOneBlock = 256;  // least cache rows per one-block matrix-core wave on small caches (measured)
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
 constexpr int kMultiWaveWavesPerCU = 8;   // multi-wave matrix-core kernel: two waves per SIMD
 constexpr int64_t kMergeBytesInKernel = 64 << 10;  // larger merges go to the combine kernel

@@ -79,7 +79,7 @@ def test_plan_grid_per_compute_unit(lib):
     one-wave workgroups per CU when a wave carries one 16-row block of a bf16
     cache, three with two blocks (MQA), four for an fp8 cache; multi-wave
     workgroups (more than 32 rows per KV head) two waves per SIMD; small
-    caches: at least 256 cache rows per one-block bf16 wave, and at most 32
+    caches: at least 256 cache rows per one-block wave, and at most 32
     pieces per segment."""
     cu = 256
     assert gqa.plan(_shape(B=32))["workgroups"] == 2 * cu                      # batched GQA-8
@@ -97,8 +97,10 @@ def test_plan_grid_per_compute_unit(lib):
     d128 = gqa.plan(_shape(B=1, G=8, D=128))
     assert d128["workgroups"] == 8 * 4096 // 256 and d128["combine"] == 0       # 18 pieces x 2 KB merged in-kernel
     assert gqa.plan(_shape(B=1, G=8, D=64, T=16384))["workgroups"] == 8 * 32    # pieces-per-segment bound
-    # the minimum applies to one-block bf16 waves only
-    assert gqa.plan(_shape(B=1, G=8, D=64, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 32
+    # an fp8 cache too; not waves carrying two query blocks (MQA)
+    assert gqa.plan(_shape(B=1, G=8, D=64, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
+    assert gqa.plan(_shape(B=1, G=8, D=128, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
+    assert gqa.plan(_shape(B=1, G=1, T=8192))["workgroups"] > 8192 // 256
 
 
 def test_plan_workgroup_option(lib):
