@@ -68,6 +68,24 @@ def test_fp8_matches_oracle(gqa, orc, case):
     assert float(np.abs(g - want).max()) <= TOL
 
 
+@pytest.mark.parametrize("B,D,lens", [(1, 128, [4096]), (2, 64, [4096, 1234])])
+def test_fp8_small_cache_default_plan(gqa, orc, B, D, lens):
+    """A small fp8 cache runs the default plan with at least 256 cache rows
+    per wave (B * 8 * 4096 / 256 workgroups) and matches the oracle."""
+    G = 8
+    x = gi.make_custom(B, 32, G, D, 4096, 1, dtype="bf16", seed=620 + B + D, seq_lens=lens)
+    kc, ks = _quantize(x["k"], G)
+    vc, vs = _quantize(x["v"], G)
+    plan = gqa.plan(gqa.shape_of(x["q"], kc))
+    assert plan["workgroups"] == B * G * 4096 // 256
+    want = orc.decode_fp8_f64(x["q"], kc, vc, ks, vs, x["seq_lens"], threads=8)
+    got = gqa.decode_fp8(x["q"].cuda(), kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda(), x["seq_lens"].cuda())
+    torch.cuda.synchronize()
+    g = got.double().cpu().numpy()
+    assert np.isfinite(g).all()
+    assert float(np.abs(g - want).max()) <= TOL
+
+
 def test_fp8_with_power_of_two_scales_is_a_bf16_cache(gqa, orc):
     B, H, G, D, T, sq = 3, 32, 8, 128, 500, 1
     x = gi.make_custom(B, H, G, D, T, sq, dtype="bf16", seed=610, seq_lens=[500, 257, 30])

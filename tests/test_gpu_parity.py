@@ -224,6 +224,22 @@ def test_merge_modes_match_oracle(gqa, orc, H, G, sq, D):
             assert torch.equal(o, _run(gqa, xc, **kw))
 
 
+@pytest.mark.parametrize("B,D,lens", [(1, 128, [4096]), (1, 64, [4096]), (2, 64, [4096, 2500]),
+                                      (3, 128, [4096, 1, 4000])])
+def test_small_cache_default_plans(gqa, orc, B, D, lens):
+    """Small caches run the default plan with at least 256 cache rows per
+    one-block wave (B * 8 * 4096 / 256 workgroups, merges in the kernel);
+    the result is the oracle's, ragged and one-row sequences included."""
+    x = gi.make_custom(B, 32, 8, D, 4096, 1, dtype="bf16", seed=900 + B + D, seq_lens=lens)
+    plan = gqa.plan(gqa.shape_of(x["q"], x["k"]))
+    assert plan["workgroups"] == B * 8 * 4096 // 256 and plan["combine"] == 0
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
+    xc = _to(x, "cuda")
+    o = _run(gqa, xc)
+    _compare(o, want, TOL["bf16"], "default plan B=%d D=%d" % (B, D))
+    assert torch.equal(o, _run(gqa, xc))
+
+
 @pytest.mark.parametrize("dt,path_name", [("f32", "valu"), ("bf16", "mfma"), ("bf16", "mfma_qk")])
 def test_more_workgroups_than_cache_rows(gqa, orc, dt, path_name):
     """A grid far larger than the work (here 10 units for 64 or 500
