@@ -54,12 +54,30 @@ def kv_elem_bytes(dtype: str) -> int:
     return 4 if dtype == "f32" else 2
 
 
+def kv_bytes(G, D, sum_len, dtype: str) -> int:
+    """K and V rows each read once: 2 * sum_b(L_b) * G * D * s ("GQA
+    (Grouped-Query Attention) 분석", section "KV cache 용량", per layer)."""
+    return 2 * sum_len * G * D * kv_elem_bytes(dtype)
+
+
+def q_bytes(B, H, D, sq, dtype: str) -> int:
+    return B * H * sq * D * kv_elem_bytes(dtype)
+
+
+def o_bytes(B, H, D, sq) -> int:
+    return B * H * sq * D * 4      # fp32 output
+
+
+def repeat_kv_bytes(B, H, D, sum_len, dtype: str) -> int:
+    """What a repeat_kv path materialises per layer for K (and again for V):
+    the cache expanded to one KV head per query head ("Same GQA, Different
+    Execution Cost Across Backends", section 2).  Never allocated here; only
+    reported beside the useful bytes."""
+    return sum_len * H * D * kv_elem_bytes(dtype)
+
+
 def useful_bytes(B, H, G, D, sq, sum_len, dtype: str) -> int:
-    s = kv_elem_bytes(dtype)
-    kv = 2 * sum_len * G * D * s
-    q = B * H * sq * D * s
-    o = B * H * sq * D * 4
-    return kv + q + o
+    return kv_bytes(G, D, sum_len, dtype) + q_bytes(B, H, D, sq, dtype) + o_bytes(B, H, D, sq)
 
 
 def flops(H, D, sq, sum_len) -> int:
@@ -93,7 +111,35 @@ def load_traffic(workload: str, sha: str):
 # ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ---------------------------------------------------------------------------
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _time_oracle(args, threads: int, seconds: float):
+    import oracle
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_f64(*args, threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return passes, el
+
+
 def cpu_baseline(x_cpu, w, sum_len, seconds: float):
+    """The float64 oracle timed on the host: the whole workload on the
+    threads this process may use (at most 16: the CPU share of one GPU on
+    the box), and single-threaded on the first sequences (a bounded sample
+    of the same workload, scaled to the whole by its useful bytes)."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -103,18 +149,23 @@ def cpu_baseline(x_cpu, w, sum_len, seconds: float):
     v = x_cpu["v"].double().numpy()
     sl = x_cpu["seq_lens"].numpy().astype(np.int32)
     scale = 1.0 / math.sqrt(w.D)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_f64(q, k, v, sl, scale, threads=threads)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    passes, el = _time_oracle((q, k, v, sl, scale), threads, seconds)
     per = el / passes
     ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype)
+    # single thread: the first nb sequences
+    nb = max(1, min(w.B, 2))
+    sl1 = sl[:nb]
+    sum1 = int(np.clip(sl1, 0, w.T).sum())
+    p1, el1 = _time_oracle((q[:nb], k[:nb], v[:nb], sl1, scale), 1, seconds)
+    ub1 = useful_bytes(nb, w.H, w.G, w.D, w.sq, sum1, w.dtype)
     return {"value": ub / per / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "whole workload (%d sequences), %d passes in %.1f s, float64, "
-                      "%d threads; %.1f ms per pass" % (w.B, passes, el, threads, per * 1e3)}
+                      "%d threads; %.1f ms per pass" % (w.B, passes, el, threads, per * 1e3),
+            "single_thread": {"value": ub1 / (el1 / p1) / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": "first %d sequence(s) (%d cache rows), %d passes in %.1f s"
+                                        % (nb, sum1, p1, el1)},
+            "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+                     "threads_used": threads}}
 
 
 def parity_spot_check(args, w, x, out, extra):

@@ -27,7 +27,7 @@ import os
 import threading
 
 __all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "plan", "workspace_bytes",
-           "paged_workspace_bytes", "version", "library_path",
+           "paged_workspace_bytes", "append_workspace_bytes", "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
            "EXPORTED_SYMBOLS"]
@@ -41,7 +41,7 @@ PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
 MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
-EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_decode_ws",
+EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_append_workspace_bytes", "gqa_decode_ws",
                     "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_append", "gqa_paged_workspace_bytes",
                     "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
@@ -107,6 +107,8 @@ def load_library():
         lib.gqa_decode.restype = ctypes.c_int
         lib.gqa_workspace_bytes.argtypes = [sp]
         lib.gqa_workspace_bytes.restype = ctypes.c_size_t
+        lib.gqa_append_workspace_bytes.argtypes = [sp]
+        lib.gqa_append_workspace_bytes.restype = ctypes.c_size_t
         lib.gqa_decode_ws.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, vp]
         lib.gqa_decode_ws.restype = ctypes.c_int
@@ -175,6 +177,11 @@ def plan(shape: Shape, path=PATH_AUTO, workgroups=0, merge=0) -> dict:
 
 def workspace_bytes(shape: Shape) -> int:
     return int(load_library().gqa_workspace_bytes(ctypes.byref(shape)))
+
+
+def append_workspace_bytes(shape: Shape) -> int:
+    """Device scratch bytes gqa_decode_append needs for ``shape``."""
+    return int(load_library().gqa_append_workspace_bytes(ctypes.byref(shape)))
 
 
 def version() -> str:

@@ -5,7 +5,7 @@
 // section "Tensor parallelism과 kernel 제약" (head dims must agree and H must
 // be a multiple of G; the cache is [batch, kv_heads, sequence, head_dim]).
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -178,6 +178,17 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     if (P > by_merge && !(big_merges && merge_req != GQA_MERGE_IN_KERNEL)) P = by_merge;
     if (wg_req > 0) P = wg_req;
     if (P > (1 << 16)) P = 1 << 16;
+    // matrix-core path: a slot holds only the live rows, min(row_block, R)
+    p->slot_rows = (p->path == gqa::Path::MFMA && R < p->row_block) ? R : p->row_block;
+    // The kernels address the partial slots with 32-bit byte offsets through
+    // a buffer resource of 2^31 - 1 bytes: cap the grid so that all of its
+    // slots fit (a larger grid would drop stores silently).  Any grid gives
+    // the same result to rounding.
+    {
+        const int64_t slot_bytes = 2 * (int64_t)gqa::slot_floats(p->slot_rows, s->D) * (int64_t)sizeof(float);
+        const int64_t max_p = (gqa::kMaxPartBytes - 256) / slot_bytes;
+        if (P > max_p) P = max_p;
+    }
     if (P < 1) P = 1;
     p->grid = s->B > 0 ? P : 0;
     // Merges by the last arriving wave read every piece's partial alone; when
@@ -194,8 +205,6 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
             return fail(GQA_ERR_UNSUPPORTED, "the combine kernel serves the MFMA path only");
         p->deferred = 1;
     }
-    // matrix-core path: a slot holds only the live rows, min(row_block, R)
-    p->slot_rows = (p->path == gqa::Path::MFMA && R < p->row_block) ? R : p->row_block;
     p->part_bytes = round_up((size_t)P * 2 * gqa::slot_floats(p->slot_rows, s->D) * sizeof(float), 256);
     p->ws_bytes = gqa::kCounterRegion + p->part_bytes;
     return GQA_OK;
@@ -212,15 +221,18 @@ gqa_status_t library_workspace(size_t need, void** out)
 {
     *out = nullptr;
     if (need == 0) return GQA_OK;
+    // test hook: report the allocation failure the next growth would meet
+    // (checked before any device call, so the path runs without a GPU too)
+    const char* inject = getenv("GQA_TEST_FAIL_ALLOC");
+    const bool fail_alloc = inject && inject[0] == '1';
     int dev = 0;
+    if (fail_alloc) return fail(GQA_ERR_ALLOC, "workspace allocation failed (injected by GQA_TEST_FAIL_ALLOC)");
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
     DeviceWorkspace& w = g_ws[dev];
     if (w.bytes < need) {
-        const char* inject = getenv("GQA_TEST_FAIL_ALLOC");
-        if (inject && inject[0] == '1') return fail(GQA_ERR_ALLOC, "workspace allocation failed (injected)");
         if (w.ptr) {
             // earlier calls on any stream may still use the old buffer
             e = hipDeviceSynchronize();
@@ -334,6 +346,13 @@ size_t gqa_workspace_bytes(const gqa_shape_t* shape)
 {
     gqa::Plan plan;
     if (make_plan(shape, nullptr, &plan) != GQA_OK) return 0;
+    return plan.ws_bytes;
+}
+
+size_t gqa_append_workspace_bytes(const gqa_shape_t* shape)
+{
+    gqa::Plan plan;
+    if (make_plan(shape, nullptr, &plan, 1) != GQA_OK) return 0;
     return plan.ws_bytes;
 }
 

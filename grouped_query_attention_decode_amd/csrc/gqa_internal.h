@@ -2,7 +2,7 @@
 // launchers (gqa_kernels.hip).  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -18,6 +18,9 @@ constexpr int kMinRowsPerWaveOneBlock = 256;  // least cache rows per one-block 
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
 constexpr int kMultiWaveWavesPerCU = 8;   // multi-wave matrix-core kernel: two waves per SIMD
 constexpr int64_t kMergeBytesInKernel = 64 << 10;  // larger merges go to the combine kernel
+// Partial slots are addressed by 32-bit byte offsets within one buffer
+// resource: their area stays below 2 GiB (the planner caps the grid).
+constexpr int64_t kMaxPartBytes = (int64_t)1 << 31;
 // The workspace starts with one arrival counter per possible segment, at a
 // fixed place whatever the shape, so counters never land on another call's
 // partials; the partials follow.
@@ -35,13 +38,13 @@ struct Plan {
     int kv_fp8;         // 1: bf16 q, fp8 E4M3 k/v codes with per-KV-head scales
     int D;
     int R;              // (H/G)*sq query rows per KV head
-    int row_block;      // rows per segment (power of two <= 16; 16 on the MFMA path)
+    int row_block;      // query rows per segment: a power of two <= 16 (vector ALU), 16, 32, 64 or 128 (MFMA)
     int n_rb;           // row blocks per (b, g)
-    int64_t grid;       // workgroups (one wave each) P
+    int64_t grid;       // workgroups P (of wg_waves waves each)
     int deferred;       // 1: split segments are merged by a second, parallel kernel
     int slot_rows;      // matrix-core path: rows per partial slot, min(row_block, R)
     int src;            // matrix-core path: 0 cache, 1 cache + appended tokens, 2 paged cache
-    int wg_waves;       // waves per workgroup: 1, or 2 / 4 for the multi-wave matrix-core kernel
+    int wg_waves;       // waves per workgroup: 1, or 4 / 8 for the multi-wave matrix-core kernel
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };
@@ -78,7 +81,15 @@ hipError_t launch_decode(const Plan& plan, const Args& args, hipStream_t stream)
 // Workgroups of the plan's kernel one compute unit can hold (0 if unknown).
 int resident_groups_per_cu(const Plan& plan);
 
-// Cache rows one wave covers per tile.
-int cache_rows_per_wave_tile(const Plan& plan);
+// Cache rows one wave covers per tile: 16 on the matrix-core paths; on the
+// vector-ALU path kSlotsPerLane rows per lane times the cache rows one
+// wave-wide 16-byte load covers.
+inline int cache_rows_per_wave_tile(const Plan& p)
+{
+    if (p.path != Path::VALU) return 16;
+    const int es = p.kv_bf16 ? 2 : 4;
+    const int lpt = p.D * es / 16;
+    return kSlotsPerLane * (kWave / lpt);
+}
 
 }  // namespace gqa

@@ -38,6 +38,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "gqa_chunkmap.h"
 #include "gqa_internal.h"
 
 namespace gqa {
@@ -246,6 +247,35 @@ __device__ __forceinline__ void wave_lds_fence()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Hand-over of a split segment's partials between workgroups.
+//  1. Each partial store carries the SC1 cache policy: it is written through
+//     to the device-coherent level (HBM side of every XCD's L2).
+//  2. s_waitcnt vmcnt(0) returns only once every memory operation of the
+//     wave is complete; for an SC1 store that is the device-coherent
+//     level's acknowledgement.
+//  3. Only then is the arrival counted: the device-scope atomic add is
+//     issued after the wait, so any wave whose add returns the last count
+//     was ordered after every earlier arrival's completed stores.
+//  4. The merge's loads carry SC1 as well: they read the device-coherent
+//     level, never a stale line of the reader's own L2; they are issued only
+//     after the atomic's result has been compared (a branch on it).
+// The hardware keeps this order for instructions in program order; the
+// compiler-only fences below keep the compiler from moving the buffer stores
+// below the wait, or the buffer loads above the atomic's result (HIP's
+// memory model says nothing about the order of a relaxed atomic and plain
+// buffer intrinsics, so the order is pinned here at both levels).
+__device__ __forceinline__ void partials_stored_before_arrival()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ void arrival_before_partial_loads()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int M>
@@ -503,6 +533,7 @@ __device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& p
         old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
     if (old != pd.npieces - 1) return;
+    arrival_before_partial_loads();
 
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
     const int i0 = ubase / EPL;
@@ -572,7 +603,7 @@ __device__ __forceinline__ void finish_piece(const Args& a, const float* row_m, 
     Pending pd;
     if (piece_output<D, RB, EPL, NAK>(a, row_m, row_l, acc, ubase, doff, qrow0, row0, R, n_rb, b, g, rb,
                                       off, L, W, P, p, &pd)) {
-        __builtin_amdgcn_s_waitcnt(0);       // own partial stores complete at device scope
+        partials_stored_before_arrival();    // own partial stores complete at device scope
         arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, ubase, doff, R, W, P);
     }
 }
@@ -1169,7 +1200,7 @@ decode_mqk(const Args a, const int R, const int n_rb)
     while (it.next(a, sm.lens, lbase, pc)) {
         Pending pd;
         if (mqk_piece<D, RB>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
-            __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
+            partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, (lane / LPT) * NAK, (lane % LPT) * EPL, R, W, P);
         }
     }
@@ -1332,40 +1363,6 @@ __device__ __forceinline__ float sum_x32(float x)
 // thousands of device-scope atomics on one address serialise.)
 // ---------------------------------------------------------------------------
 constexpr int kPieceCost = 64;   // rows a workgroup could stream while starting a piece (~3 us, measured)
-
-// floor(n / d) for 0 <= n < 2^60 and 0 < d, given r ~ 1 / d in double.
-// With the sizes the planner admits (P <= 2^16 chunks, V < 2^44 cost units)
-// the quotient stays below 2^44, so the double estimate is within 2^-7 of
-// it and off by at most one, which one integer step corrects.  (A 64-bit
-// integer division is a long software loop on the GPU, and this runs in
-// every piece's epilogue.)
-__device__ __forceinline__ long long div_floor(long long n, long long d, double r)
-{
-    long long q = (long long)((double)n * r);
-    const long long rem = n - q * d;
-    q += rem < 0 ? -1 : (rem >= d ? 1 : 0);
-    return q;
-}
-
-struct ChunkMap {
-    long long V;
-    int P;
-    double rV, rP;   // 1 / V, 1 / P
-
-    __device__ __forceinline__ long long start(int c) const { return div_floor((long long)c * V, P, rP); }
-    // the chunk holding cost unit x, 0 <= x < V
-    __device__ __forceinline__ int of(long long x) const { return (int)div_floor((x + 1) * P - 1, V, rV); }
-};
-
-__device__ __forceinline__ ChunkMap make_map(long long V, int P)
-{
-    ChunkMap m;
-    m.V = V;
-    m.P = V < P ? (int)V : P;
-    m.rV = 1.0 / (double)V;
-    m.rP = 1.0 / (double)m.P;
-    return m;
-}
 
 // Cost units of one segment of a sequence with L clamped rows.
 __device__ __forceinline__ uint32_t seg_cost(int L)
@@ -1920,6 +1917,7 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
         old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
     if (old != pd.npieces - 1) return;
+    arrival_before_partial_loads();
     const int live_rows = min(RB, R - pd.row0);
     for (int r0 = 0; r0 < live_rows; r0 += 16) {
         const int rows = min(16, live_rows - r0);
@@ -1964,7 +1962,7 @@ decode_mfa(const Args a, const int R, const int n_rb)
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
         if (mfa_piece<D, NB, SRC, KV8>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
-            __builtin_amdgcn_s_waitcnt(0);   // own partial stores complete at device scope
+            partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
     }
@@ -2236,7 +2234,7 @@ decode_mfw(const Args a, const int R, const int n_rb)
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
         if (mfw_piece<D, NW>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores complete at device scope
+            partials_stored_before_arrival();    // this wave's partial stores complete at device scope
             __syncthreads();                 // ... and every other wave's
             if (tid == 0) {
                 const int old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED,
@@ -2245,6 +2243,7 @@ decode_mfw(const Args a, const int R, const int n_rb)
                 if (sm.merge) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
+            arrival_before_partial_loads();
             if (sm.merge) {
                 const int rows = min(16, min(16 * NW, R - pd.row0) - 16 * w);
                 if (rows > 0) merge_block16<D>(a, pd, lane, 16 * w, rows, cm);
@@ -2456,14 +2455,6 @@ int resident_groups_per_cu(const Plan& p)
     return n;
 }
 
-int cache_rows_per_wave_tile(const Plan& p)
-{
-    if (p.path != Path::VALU) return 16;
-    const int es = p.kv_bf16 ? 2 : 4;
-    const int lpt = p.D * es / 16;
-    return kSlotsPerLane * (kWave / lpt);
-}
-
 typedef void (*CombineFn)(const Args, int, int, int);
 
 template <int NG>
@@ -2516,6 +2507,9 @@ hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)
         comb = pick_combine(p, ng);
         if (!comb || a.deferred != 1) return hipErrorInvalidValue;
     }
+    // an error left by unrelated earlier work would otherwise be reported
+    // as this launch's
+    (void)hipGetLastError();
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(kWave * p.wg_waves), 0, stream, a, p.R, p.n_rb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !comb) return e;

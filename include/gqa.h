@@ -40,8 +40,12 @@
  *   - seq_lens values outside [0, T] are clamped on the device.
  *
  * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
- * (F32, F32, F32) or (BF16, BF16, F32); H % G == 0; any B >= 0, sq >= 1,
- * T >= 1 with T * D < 2^31 and B * G * ceil((H/G)*sq / 16) <= 2^18.
+ * (F32, F32, F32), (BF16, BF16, F32) or (BF16, FP8_E4M3, F32) (the fp8
+ * cache through gqa_decode_fp8, or gqa_decode with unit scales); H % G == 0;
+ * any B >= 0, sq >= 1, T >= 1 with T * D < 2^31, B * H * sq * D < 2^40,
+ * (H/G) * sq <= 2^20 and B * G * (row blocks per KV head) <= 2^18, where a
+ * row block is 16 query rows on the vector-ALU path and 16, 32, 64 or 128
+ * on the matrix-core path (gqa_plan_t.row_block).
  */
 #ifndef GQA_H
 #define GQA_H
@@ -96,7 +100,9 @@ typedef struct {
     int32_t path;        /* gqa_path_t                                                 */
     int32_t workgroups;  /* workgroups of the (single, persistent) kernel; 0 = as many
                             as the GPU holds at once.  Each takes an equal share of the
-                            cache rows, so any value gives the same result to rounding. */
+                            cache rows, so any value gives the same result to rounding.
+                            Capped at 65536, and where the partial results of that many
+                            workgroups would pass 2 GiB (gqa_plan reports the grid). */
     int32_t merge;       /* gqa_merge_t: who merges a segment split over workgroups  */
     int32_t reserved[5]; /* must be zero                                               */
 } gqa_options_t;
@@ -131,6 +137,13 @@ gqa_status_t gqa_decode(const gqa_shape_t *shape, const void *q,
 
 /* Device scratch bytes gqa_decode_ws needs for this shape (0 on bad shape). */
 size_t gqa_workspace_bytes(const gqa_shape_t *shape);
+
+/* Device scratch bytes gqa_decode_append needs for this shape (0 on bad
+ * shape); it can differ from gqa_workspace_bytes, because appended tokens are
+ * planned with other row blocks and workgroups above 32 query rows per KV
+ * head.  Default options; a caller that sets workgroups in gqa_options_t
+ * needs the workspace of that grid (gqa_plan reports the plain decode's). */
+size_t gqa_append_workspace_bytes(const gqa_shape_t *shape);
 
 /*
  * gqa_decode_ws -- as gqa_decode, with a caller-owned device workspace of

@@ -238,3 +238,72 @@ def test_bad_options_rejected(lib):
     info = gqa.PlanInfo()
     assert lib.gqa_plan(ctypes.byref(s), ctypes.byref(o), ctypes.byref(info)) == \
         gqa.GQA_ERR_INVALID_ARG
+
+
+def test_grid_capped_so_partial_offsets_fit_32_bits(lib):
+    """The kernels address the partial slots with 32-bit byte offsets through
+    a 2 GiB buffer resource.  A caller-set grid large enough to push the slot
+    area past 2^31 bytes is capped (any grid gives the same result to
+    rounding), never planned into offsets that wrap."""
+    for H, G, sq, D in ((32, 8, 64, 128), (32, 1, 4, 128), (32, 1, 2, 128), (32, 1, 1, 128),
+                        (32, 8, 64, 64)):
+        s = _shape(B=64, H=H, G=G, sq=sq, D=D, T=4096)
+        p = gqa.plan(s, workgroups=65536)
+        rows = min(p["row_block"], p["rows_per_group"])
+        lse = (max(rows, 16) + 15) // 16 * 16
+        slot_bytes = 2 * (rows * D + lse) * 4
+        part = p["workspace_bytes"] - (1 << 20)
+        assert p["workgroups"] * slot_bytes < 1 << 31, (H, G, sq, D)
+        assert part < 1 << 31
+        if 65536 * slot_bytes >= 1 << 31:
+            assert p["workgroups"] == ((1 << 31) - 256) // slot_bytes
+        else:
+            assert p["workgroups"] == 65536
+    # the 128-row segments of 64 new tokens at D = 128: 16,512 floats a slot
+    assert gqa.plan(_shape(B=64, G=8, sq=64), workgroups=65536)["workgroups"] == 16256
+    # the combine kernel sizes its grid from the capped plan as well
+    p = gqa.plan(_shape(B=64, G=8, sq=64), workgroups=65536, merge=gqa.MERGE_COMBINE)
+    assert p["workgroups"] == 16256 and p["combine"] == 1
+
+
+def test_injected_workspace_allocation_failure(lib, monkeypatch):
+    """GQA_TEST_FAIL_ALLOC=1 makes the library-owned workspace report an
+    allocation failure (before any device call), which every entry point with
+    a library workspace returns as GQA_ERR_ALLOC with a message; a caller
+    workspace is not affected by the hook."""
+    s = _shape(B=32)
+    monkeypatch.setenv("GQA_TEST_FAIL_ALLOC", "1")
+    st = lib.gqa_decode(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, None)
+    assert st == gqa.GQA_ERR_ALLOC
+    assert "GQA_TEST_FAIL_ALLOC" in lib.gqa_last_error().decode()
+    st = lib.gqa_decode_ex(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, None,
+                           ctypes.c_size_t(0), None, None)
+    assert st == gqa.GQA_ERR_ALLOC
+    # a caller workspace that is too small is still the caller's error
+    st = lib.gqa_decode_ws(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, 16,
+                           ctypes.c_size_t(64), None)
+    assert st == gqa.GQA_ERR_ALLOC and "needed" in lib.gqa_last_error().decode()
+    monkeypatch.setenv("GQA_TEST_FAIL_ALLOC", "0")
+    # without the hook the same call gets past the workspace step; with no
+    # GPU it then fails at the device (GQA_ERR_HIP), never with ALLOC
+    import torch
+    if not torch.cuda.is_available():
+        st = lib.gqa_decode(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, None)
+        assert st == gqa.GQA_ERR_HIP
+
+
+def test_append_workspace_bytes(lib):
+    """Appended tokens above 32 query rows per KV head run one-wave
+    workgroups of 64-row segments, not the plain decode's multi-wave ones:
+    gqa_append_workspace_bytes reports the workspace that plan needs (equal
+    to the plain decode's where the plans agree)."""
+    for kw in (dict(B=32), dict(B=64, G=1, T=8192), dict(B=16, G=1, sq=2), dict(B=8, G=8, sq=64)):
+        s = _shape(**kw)
+        a = gqa.append_workspace_bytes(s)
+        assert a > 0
+        rows = s.H // s.G * s.sq
+        if rows <= 32:
+            assert a == gqa.workspace_bytes(s)
+    s = _shape(B=16, G=1, sq=2)
+    assert gqa.append_workspace_bytes(s) != gqa.workspace_bytes(s)
+    assert gqa.append_workspace_bytes(_shape(H=30)) == 0

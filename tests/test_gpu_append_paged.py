@@ -172,3 +172,32 @@ def test_variants_reject_fp32_and_bad_pages(gqa):
     with pytest.raises(gqa.GqaError) as ei:
         gqa.decode_paged(xb["q"].cuda(), kp, kp.clone(), bt)
     assert ei.value.status == gqa.GQA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case", [(2, 32, 1, 128, 150, 2, [150, 77]), (2, 8, 2, 128, 400, 64, [400, 70])],
+                         ids=["R64", "R256"])
+def test_append_with_caller_workspace(gqa, orc, case):
+    """gqa_append_workspace_bytes sizes a caller-owned workspace for
+    gqa_decode_append (above 32 query rows per KV head the append plans other
+    row blocks and grids than the plain decode); the result equals the one
+    with the library's workspace bit for bit, and the counters come back
+    zero so the buffer can be reused at once."""
+    B, H, G, D, T, sq, lens = case
+    x = gi.make_custom(B, H, G, D, T, sq, dtype="bf16", seed=410 + sq, seq_lens=lens)
+    gen = torch.Generator().manual_seed(411 + sq)
+    kn = torch.randn(B, G, sq, D, generator=gen).to(torch.bfloat16).cuda()
+    vn = torch.randn(B, G, sq, D, generator=gen).to(torch.bfloat16).cuda()
+    want, _, _ = orc.decode_append_f64(x["q"], kn.cpu(), vn.cpu(), x["k"], x["v"], x["seq_lens"],
+                                       1.0 / math.sqrt(D), threads=8)
+    q, sl = x["q"].cuda(), x["seq_lens"].cuda()
+    need = gqa.append_workspace_bytes(gqa.shape_of(q, x["k"]))
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for use_ws in (True, True, False):
+        kc, vc = x["k"].cuda(), x["v"].cuda()
+        outs.append(gqa.decode_append(q, kn, vn, kc, vc, sl, workspace=ws if use_ws else None))
+    torch.cuda.synchronize()
+    assert _err(outs[0], want) <= TOL
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert int(ws[: 1 << 20].view(torch.int32).abs().sum().item()) == 0

@@ -96,6 +96,50 @@ def test_workload_sampled_rows(gqa, orc, name, rows):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,rows", [
+    ("batched_b32_h32_g8_d128_t4096_ragged", (0, 11, 31)),
+    ("mqa_b64_h32_g1_d128_t8192", (5, 40)),
+    ("sweep_b16_h32_g8_d128_t16384_sq2", (2, 13)),
+    ("sweep_b16_h32_g1_d128_t16384_sq2", (1, 10)),
+    ("multitoken_b8_h32_g8_d128_t4096_sq64", (3,)),
+])
+@pytest.mark.parametrize("kind", ["spikes", "loud"])
+def test_full_length_masking_is_exact(gqa, orc, name, rows, kind):
+    """At full length the N(0,1) outputs are ~1/sqrt(L) in size, so a
+    masking or piece-boundary slip of one row moves them by ~1/L -- under
+    the 2e-3 tolerance.  Two V fields that make such a slip visible:
+    * spikes: V is zero except at rows L-sq+s and L-sq+s+1 of every
+      sequence (the last row query s sees and the first it must not), which
+      hold +-16 (s+1) (+-: alternating along D, signs differing between
+      the two rows).  A causal or ragged off-by-one moves an output by about
+      16/L * 16 >> 2e-3;
+    * loud: V ~ 32 N(0,1) everywhere, so dropping or doubling any one row
+      (at a tile, piece or segment boundary) moves an output by ~32/L."""
+    w = gi.WORKLOADS[name]
+    x = gi.make_inputs(w, device="cuda")
+    v = x["v"]
+    if kind == "spikes":
+        v.zero_()
+        sign = torch.tensor([1.0 if d % 2 == 0 else -1.0 for d in range(w.D)], device="cuda")
+        lens = x["seq_lens"].clamp(0, w.T).tolist()
+        for b, L in enumerate(lens):
+            for s in range(w.sq):
+                for j, row in enumerate((L - w.sq + s, L - w.sq + s + 1)):
+                    if 0 <= row < w.T:
+                        v[b, :, row, :] = (16.0 * (s + 1) * (1 - 2 * j) * sign).to(v.dtype)
+    else:
+        v.mul_(32)
+    got = _run(gqa, x)
+    for b in rows:
+        xb = {k: t[b:b + 1].cpu() for k, t in x.items()}
+        want = orc.decode_f64(xb["q"], xb["k"], xb["v"], xb["seq_lens"], 1.0 / math.sqrt(w.D), threads=8)
+        if kind == "spikes":
+            assert np.abs(want).max() > 100 * TOL[w.dtype]     # the spikes are seen
+        _compare(got[b:b + 1], want, TOL[w.dtype], "%s %s row %d" % (name, kind, b))
+    del x, v, got
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Shapes and edge cases at sizes that span several tiles and a ragged tail
 # ---------------------------------------------------------------------------
