@@ -120,6 +120,16 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // blocks) share each K/V tile a wave reads; a plain bf16 cache with more
     // than 64 rows uses 128-row segments (eight waves of a workgroup)
     if (p->path == gqa::Path::MFMA) p->row_block = R <= 16 ? 16 : R <= 32 ? 32 : (R <= 64 || src != 0 || fp8) ? 64 : 128;
+    // More than 32 rows of a plain bf16 cache: the 32 x 32 matrix-core kernel,
+    // segments of 64, 128 or 256 rows (workgroups of four waves, one per SIMD).
+    // GQA_MFX=0 selects the earlier 16 x 16 multi-wave kernel instead (for
+    // same-machine comparisons).
+    {
+        const char* mfx_env = getenv("GQA_MFX");
+        const int min_rows = (mfx_env && mfx_env[0] == '2') ? 16 : 32;
+        p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > min_rows && !(mfx_env && mfx_env[0] == '0')) ? 1 : 0;
+    }
+    if (p->mfx) p->row_block = R <= 32 ? 32 : R <= 64 ? 64 : R <= 128 ? 128 : 256;
     p->n_rb = (R + p->row_block - 1) / p->row_block;
     if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
         return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
@@ -141,6 +151,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // appended tokens and the paged cache were flat from 128 to 256 waves.
     if (p->path == gqa::Path::MFMA && p->row_block == 16)
         min_share = std::max<int64_t>(min_share, gqa::kMinRowsPerWaveOneBlock);
+    if (p->mfx) min_share = gqa::kMfxMinRowsPerGroup;
     // One-wave workgroups: kWavesPerCU per compute unit (fewer if they do not
     // fit) -- enough loads in flight to saturate HBM; more waves only add
     // pieces, and so partials and merges.  A matrix-core wave with one 16-row
@@ -162,6 +173,11 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
                : (p->path == gqa::Path::MFMA && p->row_block == 16) ? gqa::kWavesPerCUOneBlock
                                                                       : gqa::kWavesPerCU;
     if (p->wg_waves > 1) want = gqa::kMultiWaveWavesPerCU / p->wg_waves;
+    // the 32 x 32 kernel: one workgroup per compute unit
+    if (p->mfx) {
+        p->wg_waves = gqa::mfx_waves(p->row_block);
+        want = 1;
+    }
     int occ = gqa::resident_groups_per_cu(*p);
     if (occ <= 0 || occ > want) occ = want;
     int64_t P = (int64_t)device_compute_units() * occ;
@@ -180,6 +196,12 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     if (P > (1 << 16)) P = 1 << 16;
     // matrix-core path: a slot holds only the live rows, min(row_block, R)
     p->slot_rows = (p->path == gqa::Path::MFMA && R < p->row_block) ? R : p->row_block;
+    p->piece_cost = p->mfx ? gqa::kMfxPieceCost : gqa::kPieceCost;
+    {
+        // development override of the piece charge (tuning runs)
+        const char* pc_env = getenv("GQA_PIECE_COST");
+        if (pc_env && atoi(pc_env) >= 0 && atoi(pc_env) <= 4096) p->piece_cost = atoi(pc_env);
+    }
     // The kernels address the partial slots with 32-bit byte offsets through
     // a buffer resource of 2^31 - 1 bytes: cap the grid so that all of its
     // slots fit (a larger grid would drop stores silently).  Any grid gives
@@ -317,6 +339,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.scale_log2 = scale * 1.4426950408889634f;
     a.deferred = plan.deferred;
     a.slot_rows = plan.slot_rows;
+    a.piece_cost = plan.piece_cost;
     a.k_new = srcx.k_new;
     a.v_new = srcx.v_new;
     a.block_table = srcx.block_table;

@@ -17,6 +17,18 @@ constexpr int kWavesPerCUOneBlock = 2;  // matrix-core waves carrying one 16-row
 constexpr int kMinRowsPerWaveOneBlock = 256;  // least cache rows per one-block matrix-core wave on small caches (measured)
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
 constexpr int kMultiWaveWavesPerCU = 8;   // multi-wave matrix-core kernel: two waves per SIMD
+constexpr int kMfxMinRowsPerGroup = 256;  // least cache rows per workgroup of the 32 x 32 kernel
+// Rows' worth of streaming that starting a piece costs a workgroup (loading
+// its queries, filling the load pipeline, writing its result), charged in the
+// work split: the 16 x 16 kernels ~3 us (measured); the 32 x 32 kernel's
+// pieces are longer and start slower (measured per piece: ~15 K cycles to the
+// first tile, ~10 K to write a 256-row partial).
+constexpr int kPieceCost = 64;
+constexpr int kMfxPieceCost = 256;
+// Waves per workgroup of the 32 x 32 kernel for a segment of row_block rows
+// (32 query rows per wave): 64 rows as 2 query groups x 2 splits, one wave
+// per SIMD; 128 rows as 4 x 2 and 256 rows as 8 query groups, two per SIMD.
+inline int mfx_waves(int row_block) { return row_block <= 64 ? 4 : 8; }   // 32 rows: 4 splits
 constexpr int64_t kMergeBytesInKernel = 64 << 10;  // larger merges go to the combine kernel
 // Partial slots are addressed by 32-bit byte offsets within one buffer
 // resource: their area stays below 2 GiB (the planner caps the grid).
@@ -44,7 +56,9 @@ struct Plan {
     int deferred;       // 1: split segments are merged by a second, parallel kernel
     int slot_rows;      // matrix-core path: rows per partial slot, min(row_block, R)
     int src;            // matrix-core path: 0 cache, 1 cache + appended tokens, 2 paged cache
-    int wg_waves;       // waves per workgroup: 1, or 4 / 8 for the multi-wave matrix-core kernel
+    int piece_cost;     // matrix-core path: cost units (rows) charged for starting a piece
+    int wg_waves;       // waves per workgroup: 1, or 4 / 8 for the multi-wave matrix-core kernels
+    int mfx;            // 1: the 32 x 32 matrix-core kernel (more than 32 query rows, bf16 cache)
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };
@@ -61,6 +75,7 @@ struct Args {
     float scale_log2;   // scale * log2(e): scores kept in base-2 exponent units
     int deferred;       // leave every split segment's partials for the combine kernel
     int slot_rows;      // matrix-core path: query rows per partial slot
+    int piece_cost;     // matrix-core path: rows' worth of time a piece start costs (work split)
     // cache with appended tokens: the sq new rows of every (b, g), [B, G, sq, D]
     const void* k_new;
     const void* v_new;

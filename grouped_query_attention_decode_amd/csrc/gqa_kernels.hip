@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gqa_chunkmap.h"
 #include "gqa_internal.h"
 
@@ -1346,7 +1348,7 @@ __device__ __forceinline__ float sum_x32(float x)
 // ---------------------------------------------------------------------------
 // Work split of the matrix-core pass.  Work is counted in cost units: a
 // segment (sequence b, KV head g, row block rb) with L > 0 cache rows costs
-// kPieceCost + L -- its rows plus what starting a piece of it costs a
+// piece_cost + L -- its rows plus what starting a piece of it costs a
 // workgroup (loading its queries, filling the load pipeline, writing its
 // result).  All segments end to end span V cost units, cut into P chunks
 // with fixed boundaries, chunk c = [c V / P, (c + 1) V / P), taken by
@@ -1362,12 +1364,11 @@ __device__ __forceinline__ float sum_x32(float x)
 // handed out by a global counter -- was measured slower on every workload:
 // thousands of device-scope atomics on one address serialise.)
 // ---------------------------------------------------------------------------
-constexpr int kPieceCost = 64;   // rows a workgroup could stream while starting a piece (~3 us, measured)
-
-// Cost units of one segment of a sequence with L clamped rows.
-__device__ __forceinline__ uint32_t seg_cost(int L)
+// Cost units of one segment of a sequence with L clamped rows; pc: the
+// plan's charge for starting a piece (a.piece_cost).
+__device__ __forceinline__ uint32_t seg_cost(int L, int pc)
 {
-    return L > 0 ? (uint32_t)(L + kPieceCost) : 0u;
+    return L > 0 ? (uint32_t)(L + pc) : 0u;
 }
 
 // Partial slots of the matrix-core pass: two per chunk (slot 0 for the
@@ -1401,7 +1402,7 @@ __device__ __forceinline__ long long total_cost(const Args& a, const int* lens)
     long long tot = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        tot += wave_sum_u32(b < a.B ? seg_cost(lens_at(a, lens, b)) : 0u);
+        tot += wave_sum_u32(b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u);
     }
     return tot;
 }
@@ -1414,7 +1415,7 @@ __device__ __forceinline__ void locate(const Args& a, const int* lens, int units
     long long carry = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b)) : 0u;
+        const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u;
         const uint32_t incl = wave_incl_scan_u32(c, lane);
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
         if (hit) {
@@ -1451,11 +1452,12 @@ struct CostPieceIter {
         while (b < a.B && Vb < vE) {
             const int Lb = lens_at(a, lens, b);
             if (Lb > 0) {
-                const long long sc = (long long)Lb + kPieceCost;
+                const int pcost = a.piece_cost;
+                const long long sc = (long long)Lb + pcost;
                 if (k < 0) k = vA > Vb ? (int)((vA - Vb) / sc) : 0;
                 while (k < units) {
-                    const long long vfirst = Vb + k * sc + kPieceCost;
-                    if (vfirst - kPieceCost >= vE) return false;
+                    const long long vfirst = Vb + k * sc + pcost;
+                    if (vfirst - pcost >= vE) return false;
                     const long long ta = vA > vfirst ? vA - vfirst : 0;
                     const long long tb = vE - vfirst < Lb ? vE - vfirst : Lb;
                     const int kk = k++;
@@ -1471,7 +1473,7 @@ struct CostPieceIter {
                     }
                 }
             }
-            Vb += (long long)units * seg_cost(Lb);
+            Vb += (long long)units * seg_cost(Lb, a.piece_cost);
             ++b;
             k = -1;
         }
@@ -2253,6 +2255,536 @@ decode_mfw(const Args a, const int R, const int n_rb)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core pass on 32 x 32 tiles (v_mfma_f32_32x32x16_bf16), for groups
+// of more than 32 query rows of a bf16 cache.
+//
+// A workgroup has four waves, one per SIMD, and owns segments of
+// RB = 32 QB NQ query rows; it streams its chunk's pieces in 32-row K/V
+// tiles.  Its waves are NQ query groups x NS splits (NQ NS = 4):
+//   * a wave computes QB blocks of 32 query rows (all rows of its query
+//     group) against the tiles of its split;
+//   * the NQ waves of a split share each of its tiles: they load it once
+//     (coalesced 16-byte loads, every thread a share) into LDS;
+//   * split s takes tiles s, s + NS, s + 2 NS, ... of a piece, and at the
+//     piece's end the splits' running (max, sum, weighted V sum) merge
+//     through LDS -- so a piece spans NS times the rows a single wave would
+//     stream, and a segment is cut into NS times fewer pieces (fewer
+//     partials to write and merge).
+// NQ = 1 (up to 64 rows): every wave streams its own tiles, no barrier per
+// tile; NS = 1 (more than 128 rows): one K/V read serves 256 query rows.
+//
+// Per tile and 32-row query block (lane l: query row l % 32, k half
+// h = l / 32):
+//   S^T[t][r] = K[t][:] . Q[r][:]      A = K (row l % 32, elements
+//                                      16 s + 8 h .. + 7 at step s),
+//                                      B = Q^T (same elements of row l % 32)
+//   the accumulator gives lane l the scores of query row l % 32 at tile rows
+//   8 i + 4 h + j (index 4 i + j), so a row's max and sum need only the lane
+//   pair (l, l ^ 32);
+//   O^T[d][r] += V^T[d][t] P^T[t][r]   k step u covers tile rows 16 u ..:
+//                                      k index 8 h + e stands for tile row
+//                                      16 u + 8 (e / 4) + 4 h + e % 4 -- the
+//                                      rows whose weights lane l already
+//                                      holds (scores 8 u + e), and the rows
+//                                      two LDS transpose reads of V deliver.
+// Weights enter as bf16 hi + lo (about 16 bits), V is exact, accumulation
+// fp32 -- as in the 16 x 16 pass.
+//
+// LDS tiles are padded so that every access is free of bank conflicts and
+// every lane's addresses differ by compile-time constants: K rows are 2 D + 16
+// bytes apart (the 16 rows of an A-operand read start 4 banks apart), V rows
+// 2 D + 64 bytes apart (the 4 rows x 64 bytes a transpose read covers per 32
+// lanes start 16 banks apart); the row-contiguous stores of 16 lanes cover
+// one row.
+// ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct MfxGeom {
+    static constexpr int TR = 32;               // cache rows per tile
+    static constexpr int CPR = D / 8;           // 16-byte chunks per cache row
+    static constexpr int TILE_CH = TR * CPR;    // chunks of K (and of V) per tile
+    static constexpr int NKS = D / 16;          // k steps of the score product
+    static constexpr int NDB = D / 32;          // 32-column blocks of the weighted sum
+    static constexpr int SK = 2 * D + 16;       // K row stride in LDS (bytes)
+    static constexpr int SV = 2 * D + 64;       // V row stride in LDS (bytes)
+};
+
+template <int D>
+struct MfxTile {
+    alignas(16) char k[32 * MfxGeom<D>::SK];
+    alignas(16) char v[32 * MfxGeom<D>::SV];
+};
+
+// A wave that streams its own tiles (NQ = 1) needs one LDS buffer (its
+// accesses run in order); waves sharing tiles need two.
+template <int D, int QB, int NQ, int NS>
+struct MfxShared {
+    static constexpr int NBUF = NQ > 1 ? 2 : 1;
+    static constexpr int OS = D + 4;      // row stride (floats) of a wave's staged output rows
+    union {
+        MfxTile<D> t[NS][NBUF];
+        float out[NQ][QB * 32 * OS];      // piece end: the results, staged for coalesced stores
+    };
+    float ml[2][NS][NQ * QB * 32];        // piece merge: each row's max and sum per split
+    int lens[kLensWindow];                // clamped seq_lens[i]
+    int merge;                            // 1 when this workgroup arrived last for the current piece
+};
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// Tiles of loads in flight per thread: one per wave when each wave streams
+// its own tiles (64 registers each); two when waves share a tile (four, with
+// two waves per tile, measured slower: G = 1 sweep 42.2 -> 47.2 us, the AGPR
+// copies of the extra registers slowing every phase).
+template <int NQ>
+constexpr int mfx_reg_tiles() { return NQ == 1 ? 1 : 2; }
+
+template <int D, int QB, int NQ, int NS>
+__device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS>& sm, int R, const Piece& pc,
+                                          const ChunkMap& cm, int chunk, int n_rb, Pending* pd)
+{
+    using Gm = MfxGeom<D>;
+    constexpr int TR = Gm::TR, CPR = Gm::CPR, NKS = Gm::NKS, NDB = Gm::NDB, SK = Gm::SK, SV = Gm::SV;
+    constexpr int NBUF = MfxShared<D, QB, NQ, NS>::NBUF;
+    constexpr int RB = 32 * QB * NQ;
+    constexpr int NTG = kWave * NQ;                 // threads sharing a split's tiles
+    constexpr int NCH = (Gm::TILE_CH + NTG - 1) / NTG;   // K (and V) chunks per thread per tile
+    constexpr int NREG = mfx_reg_tiles<NQ>();
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int qs = w % NQ;                          // query group of this wave
+    const int sp = w / NQ;                          // split of this wave
+    const int gtid = qs * kWave + lane;             // thread within the split's group
+    // with D = 64 and eight query groups half of the threads have no chunk
+    auto has = [&](int j) { return Gm::TILE_CH % NTG == 0 || gtid + NTG * j < Gm::TILE_CH; };
+    const int col = lane & 31;                      // query row within a block; A-operand row
+    const int hf = lane >> 5;                       // k half
+    const int ta = pc.ta, tb = pc.tb;
+    const int row0 = pc.rb * RB;
+    const int wrow0 = qs * 32 * QB;                 // this wave's first row within the segment
+    const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
+
+    // B operands of the score product: query row wrow0 + 32 qb + col; a row
+    // past R reads the segment's first row instead (its results are never
+    // stored, and no select waits on the loaded values before the first
+    // tile's loads are issued)
+    uint4 qop[QB][NKS];
+    bool live[QB];
+    int last[QB];
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int r = row0 + wrow0 + 32 * qb + col;
+        live[qb] = r < R;
+        last[qb] = live[qb] ? pc.L - a.sq + (r % a.sq) : -1;
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.0f;
+        const char* qp = static_cast<const char*>(a.q) + (qrow0 + (live[qb] ? wrow0 + 32 * qb + col : 0)) * D * 2;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) qop[qb][s] = load16(qp + 2 * (16 * s + 8 * hf));
+    }
+    f32x16_t acc[QB][NDB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16_t{};
+
+    const int64_t slab = ((int64_t)pc.b * a.G + pc.g) * a.T * D;
+    const char* kbase = static_cast<const char*>(a.k) + slab * 2;
+    const char* vbase = static_cast<const char*>(a.v) + slab * 2;
+    const int ntile_all = (tb - ta + TR - 1) / TR;
+    const int ntile = ntile_all > sp ? (ntile_all - sp + NS - 1) / NS : 0;   // tiles of this split
+    MfxTile<D>* bufs = sm.t[sp];
+
+    // tile i of this split: cache rows ta + TR (sp + NS i) ..; chunk c =
+    // gtid + NTG j is row c / CPR, elements 8 (c % CPR) ..; rows past the
+    // piece's end re-read its last row (weight 0)
+    auto load = [&](int i, uint4* kk, uint4* vv) {
+        const int t0 = ta + TR * (sp + NS * i);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = min(gtid + NTG * j, Gm::TILE_CH - 1);
+            const int64_t off = ((int64_t)min(t0 + c / CPR, tb - 1) * D + (c % CPR) * 8) * 2;
+            kk[j] = load16_stream(kbase + off);
+            vv[j] = load16_stream(vbase + off);
+        }
+    };
+    auto stage = [&](int buf, const uint4* kk, const uint4* vv) {
+        char* kt = bufs[buf % NBUF].k;
+        char* vt = bufs[buf % NBUF].v;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (!has(j)) continue;
+            const int c = gtid + NTG * j;
+            const int r = c / CPR, cc = c % CPR;
+            *reinterpret_cast<uint4*>(kt + r * SK + cc * 16) = kk[j];
+            *reinterpret_cast<uint4*>(vt + r * SV + cc * 16) = vv[j];
+        }
+    };
+    // Scores are scaled inside the exponent: p = 2^(c s - m) with
+    // c = |scale * log2 e|, one FMA per score, and a row's maximum of c s is
+    // c times its raw maximum; a negative scale flips the sign of every query
+    // element instead (exact in bf16; applied once the first tile is in).
+    const float csc = fabsf(a.scale_log2);
+    const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+
+    // One tile: scores of every query block, one K step (A operand) at a
+    // time; then per block one online-softmax step and the weighted V sum.
+    // FULL: no row of the tile is past the piece or after the first new
+    // token, so nothing is masked (a uniform branch selects the variant: the
+    // masking costs a third of the softmax's instructions).
+    auto compute = [&](int buf, int t0, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const char* kt = bufs[buf % NBUF].k;
+        const char* vt = bufs[buf % NBUF].v;
+        f32x16_t s16q[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s16q[qb] = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const uint4 kop = *reinterpret_cast<const uint4*>(kt + col * SK + (2 * s + hf) * 16);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s16q[qb] = mfma32(kop, qop[qb][s], s16q[qb]);
+        }
+        uint32_t ph[QB][8], pl[QB][8];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float sc[16];
+            float mx;
+            if constexpr (FULL) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[v] = s16q[qb][v];
+                float m4[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    m4[k] = fmaxf(fmaxf(sc[4 * k], sc[4 * k + 1]), fmaxf(sc[4 * k + 2], sc[4 * k + 3]));
+                mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+                mx = max_x32(mx) * csc;
+            } else {
+                mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = t0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+                    sc[v] = (t < tb && t <= last[qb]) ? s16q[qb][v] : -INFINITY;
+                    mx = fmaxf(mx, sc[v]);
+                }
+                mx = max_x32(mx);
+                mx = mx == -INFINITY ? -INFINITY : mx * csc;
+            }
+            const bool need = mx > m_run[qb] + kSlack;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float al = need ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.0f;
+                m_run[qb] = need ? mx : m_run[qb];
+                l_run[qb] *= al;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[qb][db] *= al;
+            }
+            float p[16];
+            const float nm = -m_run[qb];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                // in a full tile every score and m_run are finite
+                if constexpr (FULL)
+                    p[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], csc, nm));
+                else
+                    p[v] = sc[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(sc[v], csc, nm));
+            }
+            // row sum as a tree (no 16-long chain of dependent adds)
+            float s8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s8[k] = p[2 * k] + p[2 * k + 1];
+            l_run[qb] += ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                ph[qb][q] = pack_bf16x2(p[2 * q], p[2 * q + 1]);
+                pl[qb][q] = pack_bf16x2(p[2 * q] - __uint_as_float(ph[qb][q] << 16),
+                                        p[2 * q + 1] - __uint_as_float(ph[qb][q] & 0xFFFF0000u));
+            }
+        }
+        // V^T: in each 16-lane group (h, cb) lane j addresses tile row
+        // 16 u + 4 h + j / 4 (and 8 rows on for the second read), columns
+        // 32 db + 16 cb + 4 (j % 4) ..; lane (h, cb, i) receives column
+        // 32 db + 16 cb + i of the group's four rows
+        const int j16 = lane & 15, cb = (lane >> 4) & 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ra = 16 * u + 4 * hf + (j16 >> 2);
+            const int rb2 = ra + 8;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int cl = 32 * db + 16 * cb + 4 * (j16 & 3);   // first bf16 column
+                const uint2 v0 = __builtin_bit_cast(
+                    uint2, lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + ra * SV + 2 * cl)));
+                const uint2 v1 = __builtin_bit_cast(
+                    uint2, lds_read_tr16(reinterpret_cast<const uint16_t*>(vt + rb2 * SV + 2 * cl)));
+                const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    acc[qb][db] = mfma32(va, make_uint4(ph[qb][4 * u], ph[qb][4 * u + 1], ph[qb][4 * u + 2],
+                                                        ph[qb][4 * u + 3]), acc[qb][db]);
+                    acc[qb][db] = mfma32(va, make_uint4(pl[qb][4 * u], pl[qb][4 * u + 1], pl[qb][4 * u + 2],
+                                                        pl[qb][4 * u + 3]), acc[qb][db]);
+                }
+            }
+        }
+    };
+
+    // Iteration i computes tile i from LDS buffer i % NBUF, then stages tile
+    // i + 1 (loaded NREG iterations earlier) into buffer (i + 1) % NBUF and
+    // issues the loads of tile i + 1 + NREG into the registers it freed.
+    // With NQ > 1 one barrier per tile orders each buffer's stores before
+    // its reads by the split's other waves, and its reads before the next
+    // stores into it (a wave alone needs no barrier and one buffer: its LDS
+    // accesses run in order).
+    // With NQ > 1 every wave runs the same number of iterations (the most
+    // any split has), so that all meet the same barriers; a split past its
+    // last tile stages clamped rows it never computes.
+    const int nloop = NQ > 1 ? (ntile_all + NS - 1) / NS : ntile;
+    if (nloop > 0) {
+        uint4 kr[NREG][NCH], vr[NREG][NCH];
+#pragma unroll
+        for (int u = 0; u < NREG; ++u) load(u, kr[u], vr[u]);
+        stage(0, kr[0], vr[0]);
+        load(NREG, kr[0], vr[0]);
+        // the query rows arrived before the first tile did
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                qop[qb][s] = make_uint4(qop[qb][s].x ^ qsign, qop[qb][s].y ^ qsign, qop[qb][s].z ^ qsign,
+                                        qop[qb][s].w ^ qsign);
+        if constexpr (NQ > 1) __syncthreads();
+        else wave_lds_fence();
+        for (int it = 0; it < nloop; it += 2 * NREG) {
+#pragma unroll
+            for (int u = 0; u < 2 * NREG; ++u) {
+                const int i = it + u;
+                if (i >= nloop) break;
+                if (NQ == 1 || i < ntile) {
+                    const int t0 = ta + TR * (sp + NS * i);
+                    if (t0 + TR <= tb && t0 + TR - 1 <= pc.L - a.sq)
+                        compute(i & 1, t0, std::true_type{});
+                    else
+                        compute(i & 1, t0, std::false_type{});
+                }
+                // the loads are issued on every path (rows past the piece
+                // clamp to its last row): with the same loads in flight on
+                // every path the compiler waits for exactly the oldest tile
+                // instead of draining the prefetches
+                const int nr = (u + 1) % NREG;
+                if (i + 1 < nloop) {
+                    if constexpr (NQ == 1) wave_lds_fence();   // this tile's reads stay before the next stores
+                    stage((i + 1) & 1, kr[nr], vr[nr]);
+                }
+                load(i + 1 + NREG, kr[nr], vr[nr]);
+                if constexpr (NQ > 1) __syncthreads();
+                else wave_lds_fence();
+            }
+        }
+    }
+
+    // ---- end of the piece ------------------------------------------------------
+    float l_full[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_full[qb] = sum_x32(l_run[qb]);
+    if constexpr (NS > 1) {
+        // merge the splits' running sums: every wave is past its tiles, so
+        // the tile buffers hold the merge
+        __syncthreads();
+        if (hf == 0) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                sm.ml[0][sp][(qs * QB + qb) * 32 + col] = m_run[qb];
+                sm.ml[1][sp][(qs * QB + qb) * 32 + col] = l_full[qb];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int ix = (qs * QB + qb) * 32 + col;
+            float M = -INFINITY;
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, sm.ml[0][s2][ix]);
+            float Lt = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) {
+                const float ms = sm.ml[0][s2][ix];
+                Lt += ms == -INFINITY ? 0.0f : sm.ml[1][s2][ix] * __builtin_amdgcn_exp2f(ms - M);
+            }
+            const float f = m_run[qb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[qb] - M);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[qb][db] *= f;
+            m_run[qb] = M;
+            l_full[qb] = Lt;
+        }
+        // sum the scaled accumulators over the splits, pairwise: at step st
+        // split sp (sp % 2 st == st) hands its sums to split sp - st through
+        // slot sp / (2 st) of the tile buffers
+        constexpr int SLOT = NQ * QB * NDB * 4 * kWave;   // float4 per split's accumulators
+        static_assert(((NS + 1) / 2) * SLOT * sizeof(float4) <= sizeof(sm.t), "split merge fits the tile buffers");
+        float4* mg = reinterpret_cast<float4*>(&sm.t[0][0]);
+#pragma unroll
+        for (int st = 1; st < NS; st *= 2) {
+            if (sp % (2 * st) == st) {
+                float4* dst = mg + (sp / (2 * st)) * SLOT;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dst[(((qs * QB + qb) * NDB + db) * 4 + i) * kWave + lane] =
+                                make_float4(acc[qb][db][4 * i], acc[qb][db][4 * i + 1], acc[qb][db][4 * i + 2],
+                                            acc[qb][db][4 * i + 3]);
+            }
+            __syncthreads();
+            if (sp % (2 * st) == 0 && sp + st < NS) {
+                const float4* src = mg + (sp / (2 * st)) * SLOT;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float4 x = src[(((qs * QB + qb) * NDB + db) * 4 + i) * kWave + lane];
+                            acc[qb][db][4 * i] += x.x;
+                            acc[qb][db][4 * i + 1] += x.y;
+                            acc[qb][db][4 * i + 2] += x.z;
+                            acc[qb][db][4 * i + 3] += x.w;
+                        }
+            }
+            __syncthreads();
+        }
+    }
+
+    const int c_first = cm.of(pc.off);
+    const int npieces = cm.of(pc.off + pc.L - 1) - c_first + 1;
+    // The results of the split-0 waves: a segment held by this chunk goes to
+    // out, else the piece's partial (rows divided by their sums, and their
+    // log2-sum-exp) to its slot -- device-scope stores when this launch
+    // merges it, plain ones for the combine kernel.  Each wave stages its
+    // rows in LDS (lane (col, h) holds row col, columns 32 db + 8 i + 4 h ..)
+    // and stores two whole rows per instruction.
+    if (sp == 0) {
+        constexpr int OS = MfxShared<D, QB, NQ, NS>::OS;
+        float* ob = sm.out[qs];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float inv = l_full[qb] > 0.0f ? 1.0f / l_full[qb] : 0.0f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float4*>(ob + (32 * qb + col) * OS + 32 * db + 8 * i + 4 * hf) =
+                        make_float4(acc[qb][db][4 * i] * inv, acc[qb][db][4 * i + 1] * inv,
+                                    acc[qb][db][4 * i + 2] * inv, acc[qb][db][4 * i + 3] * inv);
+        }
+        wave_lds_fence();
+        constexpr int LPR = D / 4;                      // lanes per row (one float4 each)
+        constexpr int RPI = kWave / LPR;                // rows per store instruction
+        const int rsub = lane / LPR, c4 = 4 * (lane % LPR);
+        const int live_rows = R - row0 - wrow0;         // rows of this wave below R
+        const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
+        const MSlots ms = mslots<D>(a);
+        const int mine = ms.base(chunk, cm.start(chunk) >= pc.off ? 0 : 1);
+        const int nrow = min(32 * QB, live_rows);
+        if (npieces == 1 || a.deferred) {
+            float* dst = npieces == 1 ? a.out + (qrow0 + wrow0) * D : a.part + mine + wrow0 * D;
+#pragma unroll 2
+            for (int r = rsub; r < nrow; r += RPI)
+                *reinterpret_cast<float4*>(dst + r * D + c4) = *reinterpret_cast<const float4*>(ob + r * OS + c4);
+        } else {
+#pragma unroll 2
+            for (int r = rsub; r < nrow; r += RPI) {
+                const float4 x = *reinterpret_cast<const float4*>(ob + r * OS + c4);
+                const float v4[4] = {x.x, x.y, x.z, x.w};
+                store4_coherent(part, mine + (wrow0 + r) * D + c4, v4);
+            }
+        }
+        if (npieces > 1 && hf == 0) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                if (!live[qb]) continue;
+                const float lse = l_full[qb] > 0.0f ? m_run[qb] + __log2f(l_full[qb]) : -INFINITY;
+                const int rr = wrow0 + 32 * qb + col;
+                if (a.deferred)
+                    a.part[mine + ms.lse + rr] = lse;
+                else
+                    store_coherent(part, mine + ms.lse + rr, lse);
+            }
+        }
+        wave_lds_fence();
+    }
+    // the staging area is the next piece's tile buffers
+    if constexpr (NQ > 1) __syncthreads();
+    if (npieces == 1) return false;
+    pd->seg = (pc.b * a.G + pc.g) * n_rb + pc.rb;
+    pd->p_first = c_first;
+    pd->npieces = npieces;
+    pd->off = pc.off;
+    pd->qrow0 = qrow0;
+    pd->row0 = row0;
+    return true;
+}
+
+template <int D, int QB, int NQ, int NS>
+__global__ void __launch_bounds__(kWave * NQ * NS) __attribute__((amdgpu_waves_per_eu(NQ * NS / 4, NQ * NS / 4)))
+decode_mfx(const Args a, const int R, const int n_rb)
+{
+    constexpr int NW = NQ * NS;
+    __shared__ MfxShared<D, QB, NQ, NS> sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    zero_empty_sequences<D>(a, P, p);
+    for (int i = tid; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
+    __syncthreads();
+    const int units = a.G * n_rb;
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
+    int fb;
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
+    Piece pc;
+    while (it.next(a, sm.lens, pc)) {
+        Pending pd;
+        if (mfx_piece<D, QB, NQ, NS>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
+            partials_stored_before_arrival();    // this wave's partial stores complete at device scope
+            __syncthreads();                     // ... and every other wave's
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(&a.counters[pd.seg], 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                sm.merge = old == pd.npieces - 1;
+                if (sm.merge) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            arrival_before_partial_loads();
+            if (sm.merge) {
+                const int live_rows = min(32 * QB * NQ, R - pd.row0);
+                for (int r0 = 16 * w; r0 < live_rows; r0 += 16 * NW)
+                    merge_block16<D>(a, pd, lane, r0, min(16, live_rows - r0), cm);
+            }
+            __syncthreads();                     // sm.merge is rewritten by the next piece
+        }
+    }
+}
+
 // Combine pass for a deferred plan: one wave per (segment, RW query rows)
 // of a split segment merges the rows' partials, in chunk order (the same
 // log2-sum-exp merge as the in-kernel one).  D / 4 lanes per row: a lane
@@ -2319,14 +2851,14 @@ combine_rows(const Args a, const int R, const int n_rb, const int P)
     long long before = 0, tot = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int bb = b0 + lane;
-        const uint32_t c = bb < a.B ? seg_cost(clamp_len(a.seq_lens, bb, a.T)) : 0u;
+        const uint32_t c = bb < a.B ? seg_cost(clamp_len(a.seq_lens, bb, a.T), a.piece_cost) : 0u;
         tot += wave_sum_u32(c);
         before += wave_sum_u32(bb < b ? c : 0u);
     }
     const long long units = (long long)a.G * n_rb;
     const ChunkMap cm = make_map(tot * units, P);
     // the cost-unit position of the segment's first row
-    const long long off = before * units + ((long long)g * n_rb + rb) * ((long long)L + kPieceCost) + kPieceCost;
+    const long long off = before * units + ((long long)g * n_rb + rb) * ((long long)L + a.piece_cost) + a.piece_cost;
     const int c_first = cm.of(off);
     const int npieces = cm.of(off + L - 1) - c_first + 1;
     if (npieces == 1) return;                 // written by its piece
@@ -2415,8 +2947,24 @@ static DecodeFn pick_mfa(const Plan& p)
     }
 }
 
+template <int D>
+static DecodeFn pick_mfx(int row_block)
+{
+    switch (row_block) {
+    case 32: return decode_mfx<D, 1, 1, 4>;
+    case 64: return decode_mfx<D, 1, 2, 2>;
+    case 128: return decode_mfx<D, 1, 4, 2>;
+    case 256: return decode_mfx<D, 1, 8, 1>;
+    default: return nullptr;
+    }
+}
+
 static DecodeFn pick(const Plan& p)
 {
+    if (p.path == Path::MFMA && p.mfx) {
+        if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
+        return p.D == 64 ? pick_mfx<64>(p.row_block) : pick_mfx<128>(p.row_block);
+    }
     if (p.path == Path::MFMA && p.wg_waves > 1) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
         if (p.wg_waves == 4) return p.D == 64 ? decode_mfw<64, 4> : decode_mfw<128, 4>;
@@ -2465,6 +3013,7 @@ static CombineFn pick_combine_ng(const Plan& p)
     case 32: return p.D == 64 ? combine_rows<64, 32, NG> : combine_rows<128, 32, NG>;
     case 64: return p.D == 64 ? combine_rows<64, 64, NG> : combine_rows<128, 64, NG>;
     case 128: return p.D == 64 ? combine_rows<64, 128, NG> : combine_rows<128, 128, NG>;
+    case 256: return p.D == 64 ? combine_rows<64, 256, NG> : combine_rows<128, 256, NG>;
     default: return nullptr;
     }
 }

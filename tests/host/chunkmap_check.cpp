@@ -19,8 +19,9 @@ int main()
 {
     // The planner admits at most 2^18 (sequence, KV head, row block)
     // segments, T * D < 2^31 with D >= 64 (T < 2^25), and a segment costs
-    // its rows plus 64: V <= 2^18 * (2^25 - 1 + 64).  Grids: 1 .. 2^16.
-    const long long vmax = (1LL << 18) * ((1LL << 25) - 1 + 64);
+    // its rows plus a piece charge of at most 4096: V <= 2^18 * (2^25 - 1 +
+    // 4096).  Grids: 1 .. 2^16.
+    const long long vmax = (1LL << 18) * ((1LL << 25) - 1 + 4096);
     std::vector<long long> Vs = {1, 2, 3, 7, 63, 64, 65, 255, 256, 257, 511, 512, 513, 65535, 65536, 65537,
                                  80681LL * 8 + 64 * 256, 1LL << 20, (1LL << 20) + 7, (1LL << 31) - 1, 1LL << 31,
                                  (1LL << 32) + 5, (1LL << 40) - 3, (1LL << 43) - 1, 1LL << 43, vmax - 1, vmax};

@@ -77,8 +77,9 @@ def test_plan_grid_per_compute_unit(lib):
     """One persistent workgroup grid per plan, sized per compute unit (256
     on MI355X, and the planner's count when no device is visible): two
     one-wave workgroups per CU when a wave carries one 16-row block of a bf16
-    cache, three with two blocks (MQA), four for an fp8 cache; multi-wave
-    workgroups (more than 32 rows per KV head) two waves per SIMD; small
+    cache, three with two blocks (MQA), four for an fp8 cache; one
+    workgroup per CU for more than 32 rows per KV head (the 32 x 32 kernel:
+    four or eight waves); small
     caches: at least 256 cache rows per one-block wave, and at most 32
     pieces per segment."""
     cu = 256
@@ -87,7 +88,7 @@ def test_plan_grid_per_compute_unit(lib):
     assert gqa.plan(_shape(B=64, G=1, T=8192))["workgroups"] == 3 * cu         # MQA, 32 rows
     fp8 = _shape(B=32, kv_dtype=gqa.GQA_FP8_E4M3)
     assert gqa.plan(fp8)["workgroups"] == 4 * cu
-    assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == 2 * cu  # 64 rows: 4-wave groups
+    assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == cu      # 64 rows: 4-wave groups
     assert gqa.plan(_shape(B=8, G=8, sq=64))["workgroups"] == cu               # 256 rows: 8-wave groups
     # small caches: at least 256 cache rows per one-block wave, then at most
     # 32 pieces per segment
@@ -123,9 +124,9 @@ def test_plan_row_blocks_for_large_groups(lib):
 
 
 def test_plan_matrix_path_row_blocks(lib):
-    """The matrix-core path packs 16, 32, 64 or (a plain bf16 cache) 128
-    query rows per segment, so the K/V of a group is read once for up to 128
-    rows."""
+    """The matrix-core path packs 16, 32, 64 or (a plain bf16 cache) 128 or
+    256 query rows per segment, so the K/V of a group is read once for up to
+    256 rows."""
     cases = [  # (H, G, sq) -> rows, row block, row blocks
         ((32, 8, 1), 4, 16, 1),
         ((32, 4, 2), 16, 16, 1),
@@ -133,8 +134,9 @@ def test_plan_matrix_path_row_blocks(lib):
         ((6, 1, 3), 18, 32, 1),
         ((32, 1, 2), 64, 64, 1),
         ((32, 1, 3), 96, 128, 1),
-        ((32, 8, 64), 256, 128, 2),
-        ((32, 1, 5), 160, 128, 2),
+        ((32, 8, 64), 256, 256, 1),
+        ((32, 1, 5), 160, 256, 1),
+        ((32, 1, 9), 288, 256, 2),
     ]
     for (H, G, sq), rows, rb, nrb in cases:
         p = gqa.plan(_shape(H=H, G=G, sq=sq))
@@ -259,11 +261,11 @@ def test_grid_capped_so_partial_offsets_fit_32_bits(lib):
             assert p["workgroups"] == ((1 << 31) - 256) // slot_bytes
         else:
             assert p["workgroups"] == 65536
-    # the 128-row segments of 64 new tokens at D = 128: 16,512 floats a slot
-    assert gqa.plan(_shape(B=64, G=8, sq=64), workgroups=65536)["workgroups"] == 16256
+    # the 256-row segments of 64 new tokens at D = 128: 33,024 floats a slot
+    assert gqa.plan(_shape(B=64, G=8, sq=64), workgroups=65536)["workgroups"] == 8128
     # the combine kernel sizes its grid from the capped plan as well
     p = gqa.plan(_shape(B=64, G=8, sq=64), workgroups=65536, merge=gqa.MERGE_COMBINE)
-    assert p["workgroups"] == 16256 and p["combine"] == 1
+    assert p["workgroups"] == 8128 and p["combine"] == 1
 
 
 def test_injected_workspace_allocation_failure(lib, monkeypatch):
