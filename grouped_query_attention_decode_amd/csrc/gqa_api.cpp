@@ -120,14 +120,16 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // blocks) share each K/V tile a wave reads; a plain bf16 cache with more
     // than 64 rows uses 128-row segments (eight waves of a workgroup)
     if (p->path == gqa::Path::MFMA) p->row_block = R <= 16 ? 16 : R <= 32 ? 32 : (R <= 64 || src != 0 || fp8) ? 64 : 128;
-    // More than 32 rows of a plain bf16 cache: the 32 x 32 matrix-core kernel,
-    // segments of 64, 128 or 256 rows (workgroups of four waves, one per SIMD).
-    // GQA_MFX=0 selects the earlier 16 x 16 multi-wave kernel instead (for
-    // same-machine comparisons).
+    // More than 16 rows of a plain bf16 cache: the 32 x 32 matrix-core kernel,
+    // segments of 32, 64, 128 or 256 rows (workgroups of four or eight
+    // waves).  Measured against the 16 x 16 kernels on one machine: MQA
+    // (32 rows) 57.7 -> 54.3 us, the sq = 2 sweep at G = 1 (64 rows)
+    // 43.9 -> 42.2 us, 64 new tokens (256 rows) 73.0 -> 63.4 us.
+    // GQA_MFX=0 selects the 16 x 16 kernels instead (for same-machine
+    // comparisons).
     {
         const char* mfx_env = getenv("GQA_MFX");
-        const int min_rows = (mfx_env && mfx_env[0] == '2') ? 16 : 32;
-        p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > min_rows && !(mfx_env && mfx_env[0] == '0')) ? 1 : 0;
+        p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > 16 && !(mfx_env && mfx_env[0] == '0')) ? 1 : 0;
     }
     if (p->mfx) p->row_block = R <= 32 ? 32 : R <= 64 ? 64 : R <= 128 ? 128 : 256;
     p->n_rb = (R + p->row_block - 1) / p->row_block;

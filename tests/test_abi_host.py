@@ -77,15 +77,14 @@ def test_plan_grid_per_compute_unit(lib):
     """One persistent workgroup grid per plan, sized per compute unit (256
     on MI355X, and the planner's count when no device is visible): two
     one-wave workgroups per CU when a wave carries one 16-row block of a bf16
-    cache, three with two blocks (MQA), four for an fp8 cache; one
-    workgroup per CU for more than 32 rows per KV head (the 32 x 32 kernel:
-    four or eight waves); small
+    cache, four for an fp8 cache; one workgroup per CU for more than 16 rows
+    per KV head (the 32 x 32 kernel: four or eight waves); small
     caches: at least 256 cache rows per one-block wave, and at most 32
     pieces per segment."""
     cu = 256
     assert gqa.plan(_shape(B=32))["workgroups"] == 2 * cu                      # batched GQA-8
     assert gqa.plan(_shape(B=16, G=32, sq=2, T=16384))["workgroups"] == 2 * cu  # MHA, 2 rows
-    assert gqa.plan(_shape(B=64, G=1, T=8192))["workgroups"] == 3 * cu         # MQA, 32 rows
+    assert gqa.plan(_shape(B=64, G=1, T=8192))["workgroups"] == cu             # MQA, 32 rows: 4 splits
     fp8 = _shape(B=32, kv_dtype=gqa.GQA_FP8_E4M3)
     assert gqa.plan(fp8)["workgroups"] == 4 * cu
     assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == cu      # 64 rows: 4-wave groups
@@ -98,10 +97,10 @@ def test_plan_grid_per_compute_unit(lib):
     d128 = gqa.plan(_shape(B=1, G=8, D=128))
     assert d128["workgroups"] == 8 * 4096 // 256 and d128["combine"] == 0       # 18 pieces x 2 KB merged in-kernel
     assert gqa.plan(_shape(B=1, G=8, D=64, T=16384))["workgroups"] == 8 * 32    # pieces-per-segment bound
-    # an fp8 cache too; not waves carrying two query blocks (MQA)
+    # an fp8 cache too; the 32 x 32 kernel (MQA) at least 256 rows per workgroup
     assert gqa.plan(_shape(B=1, G=8, D=64, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
     assert gqa.plan(_shape(B=1, G=8, D=128, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
-    assert gqa.plan(_shape(B=1, G=1, T=8192))["workgroups"] > 8192 // 256
+    assert gqa.plan(_shape(B=1, G=1, T=8192))["workgroups"] == 8192 // 256
 
 
 def test_plan_workgroup_option(lib):
@@ -295,8 +294,8 @@ def test_injected_workspace_allocation_failure(lib, monkeypatch):
 
 
 def test_append_workspace_bytes(lib):
-    """Appended tokens above 32 query rows per KV head run one-wave
-    workgroups of 64-row segments, not the plain decode's multi-wave ones:
+    """Appended tokens above 16 query rows per KV head run one-wave
+    workgroups of up to 64 rows, not the plain decode's 32 x 32 kernel:
     gqa_append_workspace_bytes reports the workspace that plan needs (equal
     to the plain decode's where the plans agree)."""
     for kw in (dict(B=32), dict(B=64, G=1, T=8192), dict(B=16, G=1, sq=2), dict(B=8, G=8, sq=64)):
@@ -304,8 +303,9 @@ def test_append_workspace_bytes(lib):
         a = gqa.append_workspace_bytes(s)
         assert a > 0
         rows = s.H // s.G * s.sq
-        if rows <= 32:
+        if rows <= 16:
             assert a == gqa.workspace_bytes(s)
     s = _shape(B=16, G=1, sq=2)
     assert gqa.append_workspace_bytes(s) != gqa.workspace_bytes(s)
     assert gqa.append_workspace_bytes(_shape(H=30)) == 0
+
