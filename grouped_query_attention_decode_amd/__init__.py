@@ -27,7 +27,7 @@ import os
 import threading
 
 __all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "plan", "workspace_bytes",
-           "paged_workspace_bytes", "append_workspace_bytes", "version", "library_path",
+           "paged_workspace_bytes", "append_workspace_bytes", "decode_noalloc", "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
            "EXPORTED_SYMBOLS"]
@@ -42,6 +42,7 @@ MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_append_workspace_bytes", "gqa_decode_ws",
+                    "gqa_decode_noalloc",
                     "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_append", "gqa_paged_workspace_bytes",
                     "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
@@ -115,6 +116,9 @@ def load_library():
         lib.gqa_decode_ex.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_ex.restype = ctypes.c_int
+        lib.gqa_decode_noalloc.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp,
+                                           ctypes.POINTER(Options), vp]
+        lib.gqa_decode_noalloc.restype = ctypes.c_int
         lib.gqa_decode_fp8.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                        ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_fp8.restype = ctypes.c_int
@@ -251,6 +255,32 @@ def decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
             seq_lens.data_ptr() if seq_lens is not None else None,
             ctypes.c_float(scale), out.data_ptr(), ws_ptr, ctypes.c_size_t(ws_len),
             ctypes.byref(opts), sptr)
+    _check(st)
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens=None, scale=None, out=None, *,
+                   path=PATH_AUTO, workgroups=0, merge=0, stream=None):
+    """As ``decode``, through gqa_decode_noalloc: no device memory is
+    allocated (``out`` must then be given); the library's fixed 64 MiB
+    scratch serves as workspace, so calls that overlap on one device race."""
+    import torch
+    lib = load_library()
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out")
+    out = _common_checks(q, (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)), seq_lens, out)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a shape and dtype")
+    dev = q.device
+    scale = 1.0 / math.sqrt(q.shape[3]) if scale is None else scale
+    shape = shape_of(q, k_cache, out.dtype)
+    stream = torch.cuda.current_stream(dev) if stream is None else stream
+    opts = _options(path, workgroups, merge)
+    with torch.cuda.device(dev):
+        st = lib.gqa_decode_noalloc(
+            ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr() if seq_lens is not None else None, ctypes.c_float(scale),
+            out.data_ptr(), ctypes.byref(opts), ctypes.c_void_p(stream.cuda_stream))
     _check(st)
     return out
 

@@ -297,7 +297,8 @@ struct Source {
 
 gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const void* v,
                  const int32_t* seq_lens, float scale, void* out, void* workspace, size_t ws_bytes,
-                 bool library_ws, const gqa_options_t* opts, void* stream, const Source& srcx = Source())
+                 bool library_ws, const gqa_options_t* opts, void* stream, const Source& srcx = Source(),
+                 bool fixed_scratch = false)
 {
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan, srcx.src);
@@ -315,7 +316,17 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     if (srcx.src == 1 && (!srcx.k_new || !srcx.v_new || misaligned(srcx.k_new) || misaligned(srcx.v_new)))
         return fail(GQA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL and 16-byte aligned");
     if (srcx.src == 2 && !srcx.block_table) return fail(GQA_ERR_INVALID_ARG, "block_table must be non-NULL");
-    if (library_ws) {
+    if (fixed_scratch) {
+        // the fixed device array: no allocation of any kind
+        if (plan.ws_bytes > gqa::kNoAllocScratchBytes)
+            return fail(GQA_ERR_ALLOC,
+                        "this shape needs a %zu-byte workspace, above the fixed %zu-byte scratch of "
+                        "gqa_decode_noalloc; lower options->workgroups (gqa_plan reports the size)",
+                        plan.ws_bytes, gqa::kNoAllocScratchBytes);
+        hipError_t e = gqa::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        ws_bytes = gqa::kNoAllocScratchBytes;
+    } else if (library_ws) {
         st = library_workspace(plan.ws_bytes, &workspace);
         if (st != GQA_OK) return st;
     } else if (plan.ws_bytes > 0) {
@@ -351,6 +362,13 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     a.k_scale = srcx.k_scale;
     a.v_scale = srcx.v_scale;
 
+    if (fixed_scratch) {
+        // the shared array keeps the last call's contents: clear the arrival
+        // counters this call uses (the partials need no clearing)
+        const int64_t nseg = (int64_t)shape->B * shape->G * plan.n_rb;
+        hipError_t e = gqa::launch_clear_counters(a.counters, (int)nseg, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(GQA_ERR_HIP, "clearing the counters: %s", hipGetErrorString(e));
+    }
     hipError_t e = gqa::launch_decode(plan, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
@@ -396,6 +414,13 @@ gqa_status_t gqa_decode_ex(const gqa_shape_t* shape, const void* q, const void* 
     const bool lib_ws = workspace == nullptr && ws_bytes == 0;
     return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts,
                stream);
+}
+
+gqa_status_t gqa_decode_noalloc(const gqa_shape_t* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                                const gqa_options_t* opts, void* stream)
+{
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, nullptr, 0, false, opts, stream, Source(), true);
 }
 
 gqa_status_t gqa_decode_append(const gqa_shape_t* shape, const void* q, const void* k_new, const void* v_new,

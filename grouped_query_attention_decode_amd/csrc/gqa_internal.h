@@ -93,6 +93,14 @@ struct Args {
 // Queue the decode kernel on stream.
 hipError_t launch_decode(const Plan& plan, const Args& args, hipStream_t stream);
 
+// Fixed device scratch of the entry point that allocates nothing (counters,
+// then partials), and its address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
+// Zero counters[0 .. n) on stream (a kernel, so a graph may capture it).
+hipError_t launch_clear_counters(int32_t* counters, int n, hipStream_t stream);
+
 // Workgroups of the plan's kernel one compute unit can hold (0 if unknown).
 int resident_groups_per_cu(const Plan& plan);
 

@@ -38,7 +38,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "gqa_chunkmap.h"
 #include "gqa_internal.h"
@@ -3043,6 +3045,47 @@ static CombineFn pick_combine(const Plan& p, int ng)
     case 4: return pick_combine_ng<4>(p);
     default: return nullptr;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the entry point that allocates nothing: the arrival counters and
+// partials of one call at a time per device, in a fixed device array (zero
+// when the code object loads).  Host code reaches it only through the
+// per-device address hipGetSymbolAddress returns, taken once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr)
+{
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+__global__ void __launch_bounds__(256) clear_ints(int32_t* c, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0;
+}
+
+hipError_t launch_clear_counters(int32_t* counters, int n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    (void)hipGetLastError();
+    const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(clear_ints, dim3(blocks), dim3(256), 0, stream, counters, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const Plan& p, const Args& a, hipStream_t stream)

@@ -173,6 +173,29 @@ gqa_status_t gqa_decode_ex(const gqa_shape_t *shape, const void *q,
                            const gqa_options_t *opts, void *stream);
 
 /*
+ * gqa_decode_noalloc -- gqa_decode_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): it calls no hipMalloc, hipFree or
+ * other allocating routine.  (The first call on a device looks up the
+ * array's address; make that call before any capture begins.)  Its
+ * workspace is a fixed 64 MiB device array
+ * inside libgqa, one per device, held until the process ends; a shape (and
+ * options->workgroups) whose workspace exceeds it (gqa_plan_t.
+ * workspace_bytes) is refused with GQA_ERR_ALLOC and a message -- fewer
+ * workgroups need less.  Each call first clears the arrival counters it
+ * uses with a small kernel on stream, then queues the decode as
+ * gqa_decode_ex does (same plan, same kernels, same bits).  Every call on a
+ * device shares that array: calls that may overlap on one device (other
+ * streams, or queued work not yet finished while another host thread
+ * calls) race and must be serialised by the caller.  opts may be NULL.
+ */
+gqa_status_t gqa_decode_noalloc(const gqa_shape_t *shape, const void *q,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *seq_lens, float scale,
+                                void *out, const gqa_options_t *opts,
+                                void *stream);
+
+/*
  * gqa_decode_append -- the decode step with its new tokens' K/V appended:
  * the sq new rows of every (sequence b, KV head g), k_new / v_new
  * [B, G, sq, D] (dtype of the caches), are stored into the caches at rows

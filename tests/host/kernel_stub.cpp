@@ -9,4 +9,12 @@ hipError_t launch_decode(const Plan&, const Args&, hipStream_t) { return hipErro
 
 int resident_groups_per_cu(const Plan&) { return 0; }
 
+hipError_t noalloc_scratch(void** ptr)
+{
+    *ptr = nullptr;
+    return hipErrorNoDevice;
+}
+
+hipError_t launch_clear_counters(int32_t*, int, hipStream_t) { return hipErrorNoDevice; }
+
 }  // namespace gqa

@@ -89,6 +89,18 @@ int main()
     setenv("GQA_TEST_FAIL_ALLOC", "1", 1);
     EXPECT(gqa_decode(&s, (void*)16, (void*)16, (void*)16, nullptr, 0.1f, (void*)16, nullptr) == GQA_ERR_ALLOC);
     unsetenv("GQA_TEST_FAIL_ALLOC");
+    // the entry point that allocates nothing refuses a workspace beyond its
+    // fixed scratch before touching a device
+    {
+        gqa_shape_t big = shape(64, 32, 8, 64, 4096, 128);
+        gqa_options_t o;
+        std::memset(&o, 0, sizeof(o));
+        o.workgroups = 65536;
+        EXPECT(gqa_decode_noalloc(&big, (void*)16, (void*)16, (void*)16, nullptr, 0.1f, (void*)16, &o, nullptr) ==
+               GQA_ERR_ALLOC);
+        EXPECT(gqa_decode_noalloc(nullptr, (void*)16, (void*)16, (void*)16, nullptr, 0.1f, (void*)16, &o, nullptr) ==
+               GQA_ERR_INVALID_ARG);
+    }
     // paged shapes
     gqa_paged_shape_t ps;
     std::memset(&ps, 0, sizeof(ps));

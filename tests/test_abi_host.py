@@ -309,3 +309,18 @@ def test_append_workspace_bytes(lib):
     assert gqa.append_workspace_bytes(s) != gqa.workspace_bytes(s)
     assert gqa.append_workspace_bytes(_shape(H=30)) == 0
 
+
+def test_noalloc_refuses_oversized_workspace_before_any_gpu_work(lib):
+    """gqa_decode_noalloc's workspace is a fixed 64 MiB array: a plan that
+    needs more (here 64 new tokens of 32 heads on 8 KV heads over 65536
+    workgroups) is refused with GQA_ERR_ALLOC and a message, before any
+    device call."""
+    s = _shape(B=64, G=8, sq=64)
+    o = gqa.Options()
+    o.workgroups = 65536
+    info = gqa.PlanInfo()
+    assert lib.gqa_plan(ctypes.byref(s), ctypes.byref(o), ctypes.byref(info)) == gqa.GQA_OK
+    assert info.workspace_bytes > 64 << 20
+    st = lib.gqa_decode_noalloc(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, ctypes.byref(o), None)
+    assert st == gqa.GQA_ERR_ALLOC
+    assert "scratch" in lib.gqa_last_error().decode()
