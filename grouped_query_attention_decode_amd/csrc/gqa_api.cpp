@@ -124,7 +124,10 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // segments of 32, 64, 128 or 256 rows (workgroups of four or eight
     // waves).  Measured against the 16 x 16 kernels on one machine: MQA
     // (32 rows) 57.7 -> 54.3 us, the sq = 2 sweep at G = 1 (64 rows)
-    // 43.9 -> 42.2 us, 64 new tokens (256 rows) 73.0 -> 63.4 us.
+    // 43.9 -> 42.2 us, 64 new tokens (256 rows) 73.0 -> 63.4 us.  At 16 rows
+    // or fewer the one-wave 16 x 16 kernel stays faster (batched GQA-8
+    // decode 59.3 vs 62.9 us, the sq = 2 sweep at G = 8 157 vs 171, G = 4
+    // 87.3 vs 89.6).
     // GQA_MFX=0 selects the 16 x 16 kernels instead (for same-machine
     // comparisons).
     {
