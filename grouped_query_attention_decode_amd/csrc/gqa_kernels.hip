@@ -761,8 +761,8 @@ __device__ __forceinline__ void valu_piece(const Args& a, ValuShared<FMT, D, RB>
         for (int j = 0; j < NL; ++j) {
             const int t = min(t0 + j * TPL + lrow, tb - 1);
             const int64_t o = ((int64_t)t * D + doff) * ES;
-            kk[j] = load16(kbase + o);
-            vv[j] = load16(vbase + o);
+            kk[j] = load16_stream(kbase + o);
+            vv[j] = load16_stream(vbase + o);
         }
     };
 
