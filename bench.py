@@ -108,9 +108,21 @@ def load_traffic(workload: str, sha: str):
     return t
 
 
+def kernel_name(plan):
+    """The decode kernel a plan launches (the dominant kernel of a step)."""
+    if plan["path"] != 2:
+        return {1: "decode_valu", 3: "decode_mqk"}[plan["path"]]
+    if plan["waves_per_group"] == 1:
+        return "decode_mfa"                  # one-wave 16 x 16 kernel
+    if plan["row_block"] == 16:
+        return "decode_mfs"                  # row-split workgroups of the 16 x 16 kernel
+    return "decode_mfw" if os.environ.get("GQA_MFX") == "0" else "decode_mfx"
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores
 # ---------------------------------------------------------------------------
+
 def cpu_model() -> str:
     """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
     try:
@@ -385,6 +397,7 @@ def main(argv=None):
             "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
+            "waves_per_group": plan["waves_per_group"],
             "combine_kernel": bool(plan["combine"]),
             "mode": args.mode,
         },
@@ -408,7 +421,7 @@ def main(argv=None):
         "max_abs_err_vs_oracle_b0": None,
         "roofline": {
             "bound": "hbm",
-            "kernel": {1: "decode_valu", 2: "decode_mfa", 3: "decode_mqk"}[plan["path"]],
+            "kernel": kernel_name(plan),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

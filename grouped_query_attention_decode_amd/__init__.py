@@ -77,7 +77,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
                 ("rows_per_group", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
                 ("row_block", ctypes.c_int32), ("combine", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2),
+                ("waves_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 

@@ -135,6 +135,32 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > 16 && !(mfx_env && mfx_env[0] == '0')) ? 1 : 0;
     }
     if (p->mfx) p->row_block = R <= 32 ? 32 : R <= 64 ? 64 : R <= 128 ? 128 : 256;
+    // Up to 16 query rows of a plain bf16 cache of at most 128 MB: workgroups
+    // of 2 or 4 waves that split each piece's rows (one workgroup per 128 KB
+    // of K/V, between half the compute units and all of them).  On such
+    // caches a one-wave workgroup's stream is bound by its own load latency
+    // and per-tile chain, not by HBM.  Measured per isolated call (one-wave
+    // grid -> split): B = 1, D = 64, T = 4096 (Exaone layer, 8 MB) 17.0 ->
+    // 14.6 us; B = 2 15.7 vs 18.3; B = 4 16.5 vs 18.7; B = 8 20.7 vs 23.0;
+    // B = 16 30.1 vs 32.5; D = 128: B = 1 19.1 vs 20.4, B = 2 20.9 vs 21.9,
+    // B = 4 22.7 vs 24.0 (two waves; four: 24.6), B = 8 34.0 vs 33.9, and
+    // the batched B = 32 decode (338 MB) 62.7 vs 62.5 -- so larger caches
+    // keep one-wave workgroups.  Four waves carry a 64-dim cache or up to
+    // 32 MB; two otherwise (four waves' loads in flight, 128 KB per compute
+    // unit, slowed larger 128-dim caches).  GQA_RSPLIT=0 / 2 / 4 forces the
+    // choice (same-machine comparisons).
+    p->rsplit = 0;
+    const int64_t kv_bytes = (int64_t)s->B * s->G * s->T * s->D * 2 * 2;
+    {
+        const bool eligible = p->path == gqa::Path::MFMA && !fp8 && src == 0 && p->row_block == 16;
+        const char* rs_env = getenv("GQA_RSPLIT");
+        if (eligible && rs_env && rs_env[0] != '\0') {
+            const int rs = atoi(rs_env);
+            if (rs == 2 || rs == 4) p->rsplit = rs;
+        } else if (eligible && kv_bytes <= gqa::kRowSplitMaxBytes) {
+            p->rsplit = (s->D == 64 || kv_bytes <= gqa::kRowSplitFourWaveBytes) ? 4 : 2;
+        }
+    }
     p->n_rb = (R + p->row_block - 1) / p->row_block;
     if ((int64_t)s->B * s->G * p->n_rb > gqa::kMaxSegments)
         return fail(GQA_ERR_INVALID_ARG, "B * G * ceil(R / %d) = %lld exceeds %d (sequence, KV head) segments",
@@ -183,11 +209,25 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->wg_waves = gqa::mfx_waves(p->row_block);
         want = 1;
     }
+    if (p->rsplit > 1) {
+        p->wg_waves = p->rsplit;
+        want = 1;
+    }
     int occ = gqa::resident_groups_per_cu(*p);
     if (occ <= 0 || occ > want) occ = want;
     int64_t P = (int64_t)device_compute_units() * occ;
     const int64_t by_size = (max_units + min_share - 1) / min_share;
     if (P > by_size) P = by_size;
+    if (p->rsplit > 1) {
+        // one workgroup per kRowSplitBytesPerGroup of K/V, between half the
+        // compute units and all of them, and at least a tile per wave
+        const int64_t cus = device_compute_units();
+        P = kv_bytes / gqa::kRowSplitBytesPerGroup;
+        if (P < cus / 2) P = cus / 2;
+        if (P > cus) P = cus;
+        const int64_t by_tiles = (max_units + 32 * p->rsplit - 1) / (32 * p->rsplit);
+        if (P > by_tiles) P = by_tiles;
+    }
     // A split segment merged in-kernel is merged by one wave reading every
     // piece's partial: keep the pieces per segment (at full length) bounded
     // unless the combine kernel (one wave per query row) does the merging.
@@ -520,6 +560,7 @@ gqa_status_t gqa_plan(const gqa_shape_t* shape, const gqa_options_t* opts, gqa_p
     plan->row_blocks = p.n_rb;
     plan->row_block = p.row_block;
     plan->combine = p.deferred;
+    plan->waves_per_group = p.wg_waves;
     plan->workspace_bytes = p.ws_bytes;
     return ok();
 }

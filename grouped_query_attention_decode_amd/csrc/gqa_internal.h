@@ -18,6 +18,11 @@ constexpr int kMinRowsPerWaveOneBlock = 256;  // least cache rows per one-block 
 constexpr int kMaxPiecesPerSegment = 32;  // planner bound on the split of one segment
 constexpr int kMultiWaveWavesPerCU = 8;   // multi-wave matrix-core kernel: two waves per SIMD
 constexpr int kMfxMinRowsPerGroup = 256;  // least cache rows per workgroup of the 32 x 32 kernel
+// Row-split workgroups of the 16 x 16 kernel (measured): caches up to 128 MB,
+// one workgroup per 128 KB of K/V, four waves up to 32 MB (or D = 64).
+constexpr int64_t kRowSplitMaxBytes = (int64_t)128 << 20;
+constexpr int64_t kRowSplitFourWaveBytes = (int64_t)32 << 20;
+constexpr int64_t kRowSplitBytesPerGroup = (int64_t)128 << 10;
 // Rows' worth of streaming that starting a piece costs a workgroup (loading
 // its queries, filling the load pipeline, writing its result), charged in the
 // work split: the 16 x 16 kernels ~3 us (measured); the 32 x 32 kernel's
@@ -59,6 +64,7 @@ struct Plan {
     int piece_cost;     // matrix-core path: cost units (rows) charged for starting a piece
     int wg_waves;       // waves per workgroup: 1, or 4 / 8 for the multi-wave matrix-core kernels
     int mfx;            // 1: the 32 x 32 matrix-core kernel (more than 32 query rows, bf16 cache)
+    int rsplit;         // > 1: 16 x 16 kernel with rsplit waves per workgroup splitting each piece's rows
     size_t part_bytes;  // partials: P * 2 * slot_floats(row_block, D) floats
     size_t ws_bytes;    // kCounterRegion + part_bytes
 };

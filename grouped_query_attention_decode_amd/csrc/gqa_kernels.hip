@@ -1312,6 +1312,24 @@ struct MfaShared {
     int pages[kPageWindow];             // paged cache: physical pages of the current row window
 };
 
+// Workgroup of NW waves that split each piece's cache rows (NB 16-row query
+// blocks): one V tile per wave, and the exchange area through which waves
+// 1 .. NW - 1 hand their running max, partial sums and accumulators to wave 0.
+template <int D, int NB, int NW>
+struct MfsShared {
+    static constexpr int SE = MfaShared<D>::SE;
+    static constexpr int NV = NB * (2 + 4 * (D / 16));   // floats per lane handed over
+    alignas(16) uint16_t vt[NW][32 * SE];
+    float xch[NW - 1][NV][kWave];
+    int lens[kLensWindow];              // clamped seq_lens[i]
+};
+
+template <int D>
+__device__ __forceinline__ uint16_t* wave_vt(MfaShared<D>& sm) { return sm.vt; }
+
+template <int D, int NB, int NW>
+__device__ __forceinline__ uint16_t* wave_vt(MfsShared<D, NB, NW>& sm) { return sm.vt[threadIdx.x / kWave]; }
+
 // Two floats to packed bf16 (round to nearest even), element 0 in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1)
 {
@@ -1488,10 +1506,11 @@ struct CostPieceIter {
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
-template <int D, int NB, int SRC, bool KV8>
-__device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R, int n_rb, const Piece& pc,
+template <int D, int NB, int SRC, bool KV8, int NW = 1, class SM = MfaShared<D>>
+__device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb, const Piece& pc,
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
+    static_assert(NW == 1 || (SRC == kSrcCache && !KV8), "row-split workgroups read a plain bf16 cache");
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
     constexpr int SE = MfaShared<D>::SE;
@@ -1507,7 +1526,16 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
     const int lane = threadIdx.x & (kWave - 1);
     const int col = lane & 15;           // query row of this lane within a block
     const int kg = lane >> 4;            // k group: cache rows 4 kg .. 4 kg + 3 of a tile
-    const int ta = pc.ta, tb = pc.tb;
+    // NW > 1: wave w streams tiles [n w / NW, n (w + 1) / NW) of the piece's
+    // n tiles (rows past the piece's end read as its last row, weight 0)
+    int ta = pc.ta, tb = pc.tb;
+    if constexpr (NW > 1) {
+        const int n = (pc.tb - pc.ta + TR - 1) / TR;
+        const int w = threadIdx.x / kWave;
+        ta = min(pc.tb, pc.ta + TR * (n * w / NW));
+        tb = min(pc.tb, pc.ta + TR * (n * (w + 1) / NW));
+    }
+    uint16_t* const vt = wave_vt(sm);
     const int row0 = pc.rb * RB;
     const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
 
@@ -1634,7 +1662,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
                 const int c = lane + kWave * j;
                 uint4 lo, hi;
                 fp8x16_to_bf16(vv[j], lo, hi);
-                uint16_t* dst = &sm.vt[(c / CPR) * SE + (c % CPR) * 16];
+                uint16_t* dst = &vt[(c / CPR) * SE + (c % CPR) * 16];
                 *reinterpret_cast<uint4*>(dst) = lo;
                 *reinterpret_cast<uint4*>(dst + 8) = hi;
             }
@@ -1646,7 +1674,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
 #pragma unroll
             for (int j = 0; j < NLV; ++j) {
                 const int c = lane + kWave * j;
-                *reinterpret_cast<uint4*>(&sm.vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
+                *reinterpret_cast<uint4*>(&vt[(c / CPR) * SE + (c % CPR) * 8]) = vv[j];
             }
         }
         if constexpr (SRC == kSrcAppend) {
@@ -1732,7 +1760,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
         // lane (kg, col) addresses row 4 kg + col / 4 (of each half), columns
         // 4 (col % 4) .. of each 16-column block and receives
         // V^T[col][4 kg .. 4 kg + 3] of the half
-        const uint16_t* vr = sm.vt + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
+        const uint16_t* vr = vt + (4 * kg + (col >> 2)) * SE + 4 * (col & 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * c));
@@ -1793,6 +1821,50 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, MfaShared<D>& sm, int R
                 t0 += TR;
             }
         }
+    }
+
+    if constexpr (NW > 1) {
+        // waves 1 .. NW - 1 hand (m, per-lane sum, accumulators) to wave 0,
+        // which rescales each to the common max and adds them up (a wave
+        // with no visible row has m = -inf and weight 0)
+        constexpr int NV = NB * (2 + 4 * NC);
+        static_assert(NV == SM::NV, "exchange layout");
+        const int w = threadIdx.x / kWave;
+        if (w > 0) {
+            float (*x)[kWave] = sm.xch[w - 1];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                x[nb * (2 + 4 * NC)][lane] = m_run[nb];
+                x[nb * (2 + 4 * NC) + 1][lane] = l_run[nb];
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) x[nb * (2 + 4 * NC) + 2 + 4 * c + q][lane] = acc[nb][c][q];
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+            for (int u = 0; u < NW - 1; ++u) {
+                const float (*x)[kWave] = sm.xch[u];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float mw = x[nb * (2 + 4 * NC)][lane];
+                    const float M = fmaxf(m_run[nb], mw);
+                    const float fa = m_run[nb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[nb] - M);
+                    const float fb = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                    m_run[nb] = M;
+                    l_run[nb] = l_run[nb] * fa + x[nb * (2 + 4 * NC) + 1][lane] * fb;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[nb][c][q] = acc[nb][c][q] * fa + x[nb * (2 + 4 * NC) + 2 + 4 * c + q][lane] * fb;
+                }
+            }
+        }
+        __syncthreads();                 // the exchange area is free again
+        if (w > 0) return false;
     }
 
     // ---- end of the piece ------------------------------------------------------
@@ -1966,6 +2038,45 @@ decode_mfa(const Args a, const int R, const int n_rb)
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
         if (mfa_piece<D, NB, SRC, KV8>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+            partials_stored_before_arrival();    // own partial stores complete at device scope
+            arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
+        }
+    }
+}
+
+// The same pass with NW waves per workgroup, one per SIMD, splitting every
+// piece's cache rows among them (contiguous runs of whole tiles); wave 0
+// combines the waves' results in LDS and finishes the piece.  For small
+// caches, where a one-wave workgroup's stream is bound by its own load
+// latency and per-tile chain rather than by HBM, this puts NW waves' loads in
+// flight per workgroup without adding pieces, partials or merges.
+template <int D, int NB, int NW>
+__global__ void __launch_bounds__(kWave * NW)
+decode_mfs(const Args a, const int R, const int n_rb)
+{
+    __shared__ MfsShared<D, NB, NW> sm;
+    const int P = gridDim.x;
+    const int p = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    zero_empty_sequences<D>(a, P, p);
+    for (int i = threadIdx.x; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
+    __syncthreads();
+    const int units = a.G * n_rb;
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
+    int fb;
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
+    Piece pc;
+    while (it.next(a, sm.lens, pc)) {
+        Pending pd;
+        if (mfa_piece<D, NB, kSrcCache, false, NW>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -2966,6 +3077,12 @@ static DecodeFn pick(const Plan& p)
     if (p.path == Path::MFMA && p.mfx) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
         return p.D == 64 ? pick_mfx<64>(p.row_block) : pick_mfx<128>(p.row_block);
+    }
+    if (p.path == Path::MFMA && p.rsplit > 1) {
+        if (!p.kv_bf16 || p.src != kSrcCache || p.row_block != 16 || p.wg_waves != p.rsplit) return nullptr;
+        if (p.rsplit == 2) return p.D == 64 ? decode_mfs<64, 1, 2> : decode_mfs<128, 1, 2>;
+        if (p.rsplit == 4) return p.D == 64 ? decode_mfs<64, 1, 4> : decode_mfs<128, 1, 4>;
+        return nullptr;
     }
     if (p.path == Path::MFMA && p.wg_waves > 1) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;

@@ -116,7 +116,8 @@ typedef struct {
     int32_t row_block;      /* query rows per segment                                  */
     int32_t combine;        /* 1: split segments are merged by a second kernel (one
                                wave per query row); 0: by the last arriving wave      */
-    int32_t reserved[2];
+    int32_t waves_per_group;/* waves (64 lanes) per workgroup of the kernel            */
+    int32_t reserved[1];
     uint64_t workspace_bytes; /* device scratch the call needs                        */
 } gqa_plan_t;
 

@@ -78,25 +78,46 @@ def test_plan_grid_per_compute_unit(lib):
     on MI355X, and the planner's count when no device is visible): two
     one-wave workgroups per CU when a wave carries one 16-row block of a bf16
     cache, four for an fp8 cache; one workgroup per CU for more than 16 rows
-    per KV head (the 32 x 32 kernel: four or eight waves); small
-    caches: at least 256 cache rows per one-block wave, and at most 32
-    pieces per segment."""
+    per KV head (the 32 x 32 kernel: four or eight waves); a one-block bf16
+    cache of at most 128 MB: workgroups of 4 waves (D = 64 or up to 32 MB) or
+    2 that split each piece's rows, one per 128 KB of K/V between half the
+    CUs and all of them; small caches otherwise: at least 256 cache rows per
+    one-block wave, and at most 32 pieces per segment."""
     cu = 256
-    assert gqa.plan(_shape(B=32))["workgroups"] == 2 * cu                      # batched GQA-8
+    hl = gqa.plan(_shape(B=32))                                                # batched GQA-8, 338 MB
+    assert hl["workgroups"] == 2 * cu and hl["waves_per_group"] == 1
     assert gqa.plan(_shape(B=16, G=32, sq=2, T=16384))["workgroups"] == 2 * cu  # MHA, 2 rows
     assert gqa.plan(_shape(B=64, G=1, T=8192))["workgroups"] == cu             # MQA, 32 rows: 4 splits
     fp8 = _shape(B=32, kv_dtype=gqa.GQA_FP8_E4M3)
     assert gqa.plan(fp8)["workgroups"] == 4 * cu
     assert gqa.plan(_shape(B=16, G=1, sq=2, T=16384))["workgroups"] == cu      # 64 rows: 4-wave groups
     assert gqa.plan(_shape(B=8, G=8, sq=64))["workgroups"] == cu               # 256 rows: 8-wave groups
-    # small caches: at least 256 cache rows per one-block wave, then at most
-    # 32 pieces per segment
-    ex = gqa.plan(_shape(B=1, G=8, D=64))                                       # 8 x 4096 rows
-    assert ex["workgroups"] == 8 * 4096 // 256 and ex["combine"] == 0
-    assert gqa.plan(_shape(B=2, G=8, D=64))["workgroups"] == 2 * 8 * 4096 // 256
-    d128 = gqa.plan(_shape(B=1, G=8, D=128))
-    assert d128["workgroups"] == 8 * 4096 // 256 and d128["combine"] == 0       # 18 pieces x 2 KB merged in-kernel
-    assert gqa.plan(_shape(B=1, G=8, D=64, T=16384))["workgroups"] == 8 * 32    # pieces-per-segment bound
+    # one-block bf16 caches up to 128 MB: row-split workgroups
+    def rs(**kw):
+        p = gqa.plan(_shape(**kw))
+        return p["workgroups"], p["waves_per_group"], p["combine"]
+    assert rs(B=1, G=8, D=64) == (cu // 2, 4, 0)              # Exaone layer, 8 MB
+    assert rs(B=2, G=8, D=64) == (cu // 2, 4, 0)              # 16 MB
+    assert rs(B=4, G=8, D=64) == (cu, 4, 0)                   # 32 MB
+    assert rs(B=16, G=8, D=64) == (cu, 4, 0)                  # 128 MB
+    assert rs(B=1, G=8, D=128) == (cu // 2, 4, 0)             # 16 MB
+    assert rs(B=4, G=8, D=128) == (cu, 2, 0)                  # 64 MB: two waves
+    assert rs(B=8, G=8, D=128) == (cu, 2, 0)                  # 128 MB
+    assert rs(B=9, G=8, D=128)[1] == 1                        # above 128 MB: one-wave groups
+    assert rs(B=1, G=8, D=64, T=64)[0] == 8 * 64 // (32 * 4)  # at least a tile per wave
+    # a one-wave grid on small caches otherwise: at least 256 cache rows per
+    # one-block wave, then at most 32 pieces per segment (forced here)
+    import os
+    os.environ["GQA_RSPLIT"] = "0"
+    try:
+        ex = gqa.plan(_shape(B=1, G=8, D=64))                                   # 8 x 4096 rows
+        assert ex["workgroups"] == 8 * 4096 // 256 and ex["combine"] == 0 and ex["waves_per_group"] == 1
+        assert gqa.plan(_shape(B=2, G=8, D=64))["workgroups"] == 2 * 8 * 4096 // 256
+        d128 = gqa.plan(_shape(B=1, G=8, D=128))
+        assert d128["workgroups"] == 8 * 4096 // 256 and d128["combine"] == 0   # 18 pieces x 2 KB merged in-kernel
+        assert gqa.plan(_shape(B=1, G=8, D=64, T=16384))["workgroups"] == 8 * 32  # pieces-per-segment bound
+    finally:
+        del os.environ["GQA_RSPLIT"]
     # an fp8 cache too; the 32 x 32 kernel (MQA) at least 256 rows per workgroup
     assert gqa.plan(_shape(B=1, G=8, D=64, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
     assert gqa.plan(_shape(B=1, G=8, D=128, kv_dtype=gqa.GQA_FP8_E4M3))["workgroups"] == 8 * 4096 // 256
@@ -107,9 +128,13 @@ def test_plan_workgroup_option(lib):
     p = gqa.plan(_shape(), workgroups=100)
     assert p["workgroups"] == 100
     small = gqa.plan(_shape(B=1, T=100))
-    # a tiny cache gets no more workgroups than it has shares of 256 rows:
-    # 8 KV heads x 100 rows / 256
-    assert small["workgroups"] == 4
+    # a tiny cache gets no more row-split workgroups than it has 32-row tiles
+    # per wave: 8 KV heads x 100 rows / (4 waves x 32)
+    assert small["workgroups"] == 7 and small["waves_per_group"] == 4
+    small = gqa.plan(_shape(B=1, T=100, q_dtype=gqa.GQA_F32, kv_dtype=gqa.GQA_F32))
+    # ... and the vector-ALU path no more one-wave workgroups than it has
+    # shares of two tiles (8 rows of 128 fp32 values each): 8 x 100 / 16
+    assert small["workgroups"] == 50 and small["waves_per_group"] == 1
 
 
 def test_plan_row_blocks_for_large_groups(lib):

@@ -268,20 +268,46 @@ def test_merge_modes_match_oracle(gqa, orc, H, G, sq, D):
             assert torch.equal(o, _run(gqa, xc, **kw))
 
 
-@pytest.mark.parametrize("B,D,lens", [(1, 128, [4096]), (1, 64, [4096]), (2, 64, [4096, 2500]),
-                                      (3, 128, [4096, 1, 4000])])
-def test_small_cache_default_plans(gqa, orc, B, D, lens):
-    """Small caches run the default plan with at least 256 cache rows per
-    one-block wave (B * 8 * 4096 / 256 workgroups, merges in the kernel);
-    the result is the oracle's, ragged and one-row sequences included."""
+@pytest.mark.parametrize("B,D,lens,grid,waves", [(1, 128, [4096], 128, 4), (1, 64, [4096], 128, 4),
+                                                 (2, 64, [4096, 2500], 128, 4),
+                                                 (3, 128, [4096, 1, 4000], 256, 2)])
+def test_small_cache_default_plans(gqa, orc, B, D, lens, grid, waves):
+    """Small caches run the default plan: workgroups of 4 or 2 waves that
+    split each piece's rows, one per 128 KB of K/V between half the compute
+    units and all of them, merges in the kernel; the result is the oracle's,
+    ragged and one-row sequences included."""
     x = gi.make_custom(B, 32, 8, D, 4096, 1, dtype="bf16", seed=900 + B + D, seq_lens=lens)
     plan = gqa.plan(gqa.shape_of(x["q"], x["k"]))
-    assert plan["workgroups"] == B * 8 * 4096 // 256 and plan["combine"] == 0
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert plan["workgroups"] == grid * cu // 256 and plan["waves_per_group"] == waves and plan["combine"] == 0
     want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
     xc = _to(x, "cuda")
     o = _run(gqa, xc)
     _compare(o, want, TOL["bf16"], "default plan B=%d D=%d" % (B, D))
     assert torch.equal(o, _run(gqa, xc))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("waves", [2, 4])
+@pytest.mark.parametrize("sq", [1, 2])
+def test_row_split_workgroups(gqa, orc, monkeypatch, D, waves, sq):
+    """Workgroups whose waves split each piece's cache rows: the oracle's
+    result at grids where some waves get no tile of a piece (3 workgroups
+    over a one-row sequence), pieces a few tiles long, and one workgroup per
+    compute unit, with the in-kernel merge and the combine kernel; the same
+    bits on a second call."""
+    monkeypatch.setenv("GQA_RSPLIT", str(waves))
+    x = gi.make_custom(3, 32, 8, D, 777, sq, dtype="bf16", seed=40 + D + waves + sq,
+                       seq_lens=[777, 1, 300])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(D))
+    xc = _to(x, "cuda")
+    assert gqa.plan(gqa.shape_of(xc["q"], xc["k"]))["waves_per_group"] == waves
+    for P in (3, 37, 256):
+        for m in (gqa.MERGE_IN_KERNEL, gqa.MERGE_COMBINE):
+            kw = dict(workgroups=P, merge=m)
+            o = _run(gqa, xc, **kw)
+            _compare(o, want, TOL["bf16"], "waves=%d P=%d merge=%d" % (waves, P, m))
+            assert torch.equal(o, _run(gqa, xc, **kw))
 
 
 @pytest.mark.parametrize("dt,path_name", [("f32", "valu"), ("bf16", "mfma"), ("bf16", "mfma_qk")])
