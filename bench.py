@@ -40,7 +40,7 @@ METRIC = "GQA decode attention µs/step + achieved KV-read HBM GB/s (% of peak)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_decode_amd", "csrc", f)
-                  for f in ("gqa_kernels.hip", "gqa_api.cpp", "gqa_internal.h")]
+                  for f in ("gqa_kernels.hip", "gqa_api.cpp", "gqa_internal.h", "gqa_chunkmap.h")]
 
 
 def log(*a):
@@ -93,6 +93,70 @@ def kernel_source_sha() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _counter_rows(run_dir: str, counter: str) -> dict:
+    """Per-kernel values of one counter from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    out = {}
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def write_traffic_record(args) -> int:
+    """profiles/traffic_<workload>[_<mode>].json from two rocprofv3 --pmc runs
+    of this benchmark with --copy-probe (FETCH_SIZE, then WRITE_SIZE): the
+    decode kernel's KiB per dispatch, each scaled by what the same counter
+    reads for the 1 GiB device copy (1 GiB read, 1 GiB written)."""
+    fetch_dir, write_dir = args.traffic_record
+    fe = _counter_rows(fetch_dir, "FETCH_SIZE")
+    wr = _counter_rows(write_dir, "WRITE_SIZE")
+    ours = [k for k in fe if "gqa::" in k]
+    kn = max(ours, key=lambda k: sum(fe[k]) / len(fe[k]))      # the dominant (decode) kernel
+    cp = [k for k in fe if "copyBuffer" in k]
+    if len(cp) != 1 or cp[0] not in wr or kn not in wr:
+        raise SystemExit("expected one copy kernel and the decode kernel in both runs")
+    kib = 1 << 20                                               # the copy moves 1 GiB each way
+    cf, cw = max(fe[cp[0]]), max(wr[cp[0]])
+    rs, ws = kib / cf, kib / cw
+    f = sum(fe[kn]) / len(fe[kn])
+    w = sum(wr[kn]) / len(wr[kn])
+    name = args.workload if args.mode == "decode" else "%s_%s" % (args.workload, args.mode)
+    extra = "" if args.mode == "decode" else " --mode %s" % args.mode
+    rec = {
+        "kernel": kn.split("(")[0].replace("void ", "").replace("gqa::", ""),
+        "workload": name,
+        "kernel_source_sha": kernel_source_sha(),
+        "dispatches": len(fe[kn]),
+        "fetch_size_kib_per_dispatch": f,
+        "write_size_kib_per_dispatch": w,
+        "read_scale": rs,
+        "write_scale": ws,
+        "calibration": "1 GiB device copy (%s): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB for %d KiB "
+                       "each way" % (cp[0].split("(")[0], cf, cw, kib),
+        "hbm_bytes_per_launch": int(round((f * rs + w * ws) * 1024)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o run -- python3 bench.py --no-cpu "
+            "--steps 5 --warmup 1 --copy-probe --workload %s%s" % (fetch_dir, args.workload, extra),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o run -- python3 bench.py --no-cpu "
+            "--steps 5 --warmup 1 --copy-probe --workload %s%s" % (write_dir, args.workload, extra),
+            "python3 bench.py --workload %s%s --traffic-record %s %s" % (args.workload, extra, fetch_dir,
+                                                                         write_dir)],
+    }
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+    return 0
 
 
 def load_traffic(workload: str, sha: str):
@@ -227,7 +291,12 @@ def main(argv=None):
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy (bandwidth reference, "
                          "and the calibration kernel for HBM byte counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: write profiles/traffic_<workload>.json from two rocprofv3 "
+                         "--pmc runs of this command with --copy-probe (FETCH_SIZE, then WRITE_SIZE)")
     args = ap.parse_args(argv)
+    if args.traffic_record:
+        return write_traffic_record(args)
 
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
