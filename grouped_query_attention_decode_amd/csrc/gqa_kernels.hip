@@ -1474,7 +1474,8 @@ struct CostPieceIter {
             if (Lb > 0) {
                 const int pcost = a.piece_cost;
                 const long long sc = (long long)Lb + pcost;
-                if (k < 0) k = vA > Vb ? (int)((vA - Vb) / sc) : 0;
+                // first piece of this sequence in the chunk (exact; no 64-bit division)
+                if (k < 0) k = vA > Vb ? (int)div_floor(vA - Vb, sc, 1.0 / (double)sc) : 0;
                 while (k < units) {
                     const long long vfirst = Vb + k * sc + pcost;
                     if (vfirst - pcost >= vE) return false;
