@@ -313,15 +313,16 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int lane)
 // Equal-work schedule.  Work units: cache rows of all segments, segments in
 // order (b, g, row block).  Workgroup p owns units [start(p), start(p+1)).
 // ---------------------------------------------------------------------------
+// (Exact quotients by div_floor: no 64-bit integer division on the GPU.)
 __device__ __forceinline__ long long wg_start(long long W, int P, int p)
 {
-    return (long long)p * W / P;
+    return div_floor((long long)p * W, P, 1.0 / (double)P);
 }
 
 // The workgroup whose range holds unit x (0 <= x < W).
 __device__ __forceinline__ int wg_of(long long x, long long W, int P)
 {
-    return (int)(((x + 1) * P - 1) / W);
+    return (int)div_floor((x + 1) * P - 1, W, 1.0 / (double)W);
 }
 
 // This workgroup's share of the work; every lane holds the same values.
