@@ -27,7 +27,8 @@ import os
 import threading
 
 __all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "plan", "workspace_bytes",
-           "paged_workspace_bytes", "append_workspace_bytes", "decode_noalloc", "version", "library_path",
+           "paged_workspace_bytes", "append_workspace_bytes", "decode_noalloc", "workspace_clear",
+           "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
            "MERGE_AUTO", "MERGE_IN_KERNEL", "MERGE_COMBINE",
            "EXPORTED_SYMBOLS"]
@@ -42,7 +43,7 @@ MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_append_workspace_bytes", "gqa_decode_ws",
-                    "gqa_decode_noalloc",
+                    "gqa_workspace_clear", "gqa_decode_noalloc",
                     "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_append", "gqa_paged_workspace_bytes",
                     "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
@@ -113,6 +114,8 @@ def load_library():
         lib.gqa_decode_ws.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, vp]
         lib.gqa_decode_ws.restype = ctypes.c_int
+        lib.gqa_workspace_clear.argtypes = [vp, ctypes.c_size_t, vp]
+        lib.gqa_workspace_clear.restype = ctypes.c_int
         lib.gqa_decode_ex.argtypes = [sp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_ex.restype = ctypes.c_int
@@ -181,6 +184,21 @@ def plan(shape: Shape, path=PATH_AUTO, workgroups=0, merge=0) -> dict:
 
 def workspace_bytes(shape: Shape) -> int:
     return int(load_library().gqa_workspace_bytes(ctypes.byref(shape)))
+
+
+def workspace_clear(workspace, stream=None):
+    """Zero the arrival counters of a caller workspace (a uint8 GPU tensor)
+    on ``stream`` (default: torch's current stream): before its first use,
+    or after queued work on it did not complete."""
+    import torch
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device)
+    with torch.cuda.device(workspace.device):
+        _check(load_library().gqa_workspace_clear(
+            workspace.data_ptr(), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            ctypes.c_void_p(stream.cuda_stream)))
 
 
 def append_workspace_bytes(shape: Shape) -> int:

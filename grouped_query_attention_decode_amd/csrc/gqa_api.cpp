@@ -450,6 +450,19 @@ gqa_status_t gqa_decode_ws(const gqa_shape_t* shape, const void* q, const void* 
                stream);
 }
 
+gqa_status_t gqa_workspace_clear(void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!workspace) return fail(GQA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < gqa::kCounterRegion)
+        return fail(GQA_ERR_INVALID_ARG, "ws_bytes (%zu) is below the %zu-byte counter region of every workspace",
+                    ws_bytes, (size_t)gqa::kCounterRegion);
+    const hipError_t e = gqa::launch_clear_counters(static_cast<int32_t*>(workspace),
+                                                    (int)(gqa::kCounterRegion / sizeof(int32_t)),
+                                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "clearing the workspace counters: %s", hipGetErrorString(e));
+    return ok();
+}
+
 gqa_status_t gqa_decode_ex(const gqa_shape_t* shape, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* seq_lens, float scale, void* out,
                            void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)

@@ -162,6 +162,21 @@ gqa_status_t gqa_decode_ws(const gqa_shape_t *shape, const void *q,
                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gqa_workspace_clear -- zero the arrival-counter region (the first 1 MiB)
+ * of a caller-owned workspace, asynchronously on stream, with a fill kernel
+ * (no allocation, no memset node: a graph may capture it).  Use it in place
+ * of the one-time zero fill before a workspace's first use, or to make a
+ * workspace usable again after queued work on it did not run to completion
+ * (a failed or abandoned launch can leave counters non-zero, and a later
+ * merge would then be wrong).  The partial-result region needs no clearing.
+ * workspace: device pointer; ws_bytes: its size, at least the 1 MiB counter
+ * region (gqa_workspace_bytes is always larger).  Errors: INVALID_ARG for a
+ * NULL workspace or ws_bytes below the counter region; HIP if the launch
+ * fails.  Ordering and sharing rules are those of gqa_decode_ws.
+ */
+gqa_status_t gqa_workspace_clear(void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * gqa_decode_ex -- as gqa_decode_ws with tuning options (may be NULL).
  * Results for a given input are deterministic for a given plan; different
  * workgroup counts agree to rounding.  workspace NULL with ws_bytes 0

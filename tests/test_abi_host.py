@@ -229,6 +229,15 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert st == gqa.GQA_ERR_INVALID_ARG
 
 
+def test_workspace_clear_argument_checks(lib):
+    """gqa_workspace_clear refuses a NULL workspace and one smaller than the
+    1 MiB counter region, before any device call."""
+    st = lib.gqa_workspace_clear(None, ctypes.c_size_t(1 << 20), None)
+    assert st == gqa.GQA_ERR_INVALID_ARG and "NULL" in lib.gqa_last_error().decode()
+    st = lib.gqa_workspace_clear(256, ctypes.c_size_t((1 << 20) - 4), None)
+    assert st == gqa.GQA_ERR_INVALID_ARG and "counter region" in lib.gqa_last_error().decode()
+
+
 def test_non_finite_scale_rejected(lib):
     s = _shape()
     for bad in (float("nan"), float("inf")):

@@ -338,6 +338,21 @@ def test_explicit_workspace_matches_library_workspace(gqa):
     assert int(ws[:1 << 20].view(torch.int32).abs().sum().item()) == 0
 
 
+def test_workspace_clear_makes_a_dirty_workspace_usable(gqa):
+    """A caller workspace whose counters hold garbage (as after work that did
+    not complete) gives the library workspace's bits once gqa_workspace_clear
+    has run on the stream, and is left with zeroed counters."""
+    w = gi.WORKLOADS["batched_b32_h32_g8_d128_t4096_ragged"].scaled(B=8, seed=81)
+    xc = gi.make_inputs(w, device="cuda")
+    need = gqa.workspace_bytes(gqa.shape_of(xc["q"], xc["k"]))
+    ws = torch.full((need,), 7, dtype=torch.uint8, device="cuda")
+    want = _run(gqa, xc)
+    gqa.workspace_clear(ws)
+    assert int(ws[:1 << 20].view(torch.int32).abs().sum().item()) == 0
+    assert torch.equal(_run(gqa, xc, workspace=ws), want)
+    assert int(ws[:1 << 20].view(torch.int32).abs().sum().item()) == 0
+
+
 def test_no_repeated_kv_is_allocated(gqa):
     """The only device memory the library takes is its workspace, far below
     the n_rep-times repeated K/V copy an eager repeat_kv path would make."""
