@@ -2,7 +2,9 @@
 C ABI: two calls in a row -- the second with a smaller input -- each give
 the bits of gqa_decode_ex with the same options on the same inputs, and
 match the float64 oracle within the bf16 tolerance (2e-3).  No device memory
-is allocated by the calls."""
+is allocated by the calls.  Then the same entry point, and a caller
+workspace's gqa_workspace_clear + decode, captured in HIP graphs and
+replayed."""
 import ctypes
 import math
 
@@ -89,3 +91,67 @@ def test_noalloc_refuses_a_workspace_beyond_its_scratch(gqa):
     want = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"])
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+# HIP graph capture: the callers this entry point is for.  Replays give the
+# eager call's bits, with other eager work -- including eager calls that
+# share the scratch -- between replays (no memset node is recorded: the
+# counters are cleared by a kernel).
+
+def _inputs(B, H, G, D, T, seq_lens, seed):
+    return gi.make_custom(B, H, G, D, T, 1, dtype="bf16", seed=seed, seq_lens=seq_lens, device="cuda")
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=8, H=32, G=1, D=128, T=2048, seq_lens=[2048, 1900, 1500, 1024, 700, 333, 64, 1]),   # 32 rows: combine kernel
+    dict(B=4, H=32, G=8, D=64, T=1024, seq_lens=[1024, 1000, 517, 0]),                        # 4 rows, row-split, in-kernel merge
+], ids=["mqa_like", "gqa8_small"])
+def test_noalloc_graph_replays(gqa, case):
+    x = _inputs(case["B"], case["H"], case["G"], case["D"], case["T"], case["seq_lens"], 700 + case["D"])
+    y = _inputs(case["B"], case["H"], case["G"], case["D"], case["T"], case["seq_lens"][::-1], 800 + case["D"])
+    want = gqa.decode_noalloc(x["q"], x["k"], x["v"], x["seq_lens"],    # first call: scratch address resolved
+                              out=torch.empty(x["q"].shape, dtype=torch.float32, device="cuda"))
+    want_y = gqa.decode_noalloc(y["q"], y["k"], y["v"], y["seq_lens"],
+                                out=torch.empty(y["q"].shape, dtype=torch.float32, device="cuda"))
+    # the eager library-workspace call agrees to rounding (same plan: same bits)
+    assert torch.equal(gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"]), want)
+    torch.cuda.synchronize()
+    out = torch.full_like(want, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gqa.decode_noalloc(x["q"], x["k"], x["v"], x["seq_lens"], out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqa.decode_noalloc(x["q"], x["k"], x["v"], x["seq_lens"], out=out)
+    for r in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), "replay %d" % r
+        # an eager call with other inputs shares the scratch between replays
+        oy = torch.empty_like(want_y)
+        assert torch.equal(gqa.decode_noalloc(y["q"], y["k"], y["v"], y["seq_lens"], out=oy), want_y)
+        torch.cuda.synchronize()
+
+
+def test_workspace_clear_and_decode_in_a_graph(gqa):
+    x = _inputs(4, 32, 8, 128, 1536, [1536, 1200, 77, 1], 901)
+    want = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"])
+    need = gqa.workspace_bytes(gqa.shape_of(x["q"], x["k"]))
+    ws = torch.full((need,), 5, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(want)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqa.workspace_clear(ws)
+        gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], out=out, workspace=ws)
+    for r in range(4):
+        out.fill_(float("nan"))
+        ws[: 1 << 20].fill_(3)                # garbage counters before every replay
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), "replay %d" % r
+        assert int(ws[: 1 << 20].view(torch.int32).abs().sum().item()) == 0
