@@ -284,6 +284,9 @@ def main(argv=None):
                          "randomly ordered page pool; fp8: gqa_decode_fp8 over E4M3 codes with "
                          "per-KV-head scales (amax / 448)")
     ap.add_argument("--page-size", type=int, default=16)
+    ap.add_argument("--flush-mib", type=int, default=FLUSH_BYTES >> 20,
+                    help="size of the read sweep before every step, in MiB (at least twice the "
+                         "256 MB Infinity Cache)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep (warm-cache numbers; not HBM rates)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -297,6 +300,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.traffic_record:
         return write_traffic_record(args)
+    if not args.no_flush and args.flush_mib < 512:
+        print("--flush-mib must be at least 512 (twice the 256 MB Infinity Cache)", file=sys.stderr)
+        return 2
 
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -328,7 +334,8 @@ def main(argv=None):
     plan = gqa.plan(shape, path=path, workgroups=args.workgroups, merge=merge)
     log("[bench] plan %s" % plan)
     out = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    flush_bytes = args.flush_mib << 20
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     stream = torch.cuda.current_stream(dev)
 
     if args.mode == "append":
@@ -463,7 +470,7 @@ def main(argv=None):
             "sq": w.sq, "seq_lens": ("uniform [%d, %d], seed %d" % (w.ragged[0], w.ragged[1], w.seed)
                                      if w.ragged else "all T"),
             "sum_seq_lens": sum_len, "kv_dtype": w.dtype, "out_dtype": "f32",
-            "cache": "no sweep (warm)" if args.no_flush else "1 GiB read sweep before each step",
+            "cache": "no sweep (warm)" if args.no_flush else "%d MiB read sweep before each step" % args.flush_mib,
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
             "waves_per_group": plan["waves_per_group"],
@@ -484,9 +491,9 @@ def main(argv=None):
         # the cache sweeps timed alone are a measured read-bandwidth probe: a
         # 1 GiB fp32 sum (torch's reduction kernel) per sweep
         "read_probe": (None if args.no_flush else {
-            "bytes": FLUSH_BYTES, "us": round(swp_ms / K * 1e3, 2),
-            "gbs": round(FLUSH_BYTES / (swp_ms / K * 1e-3) / 1e9, 1),
-            "kernel": "torch sum over a 1 GiB fp32 tensor"}),
+            "bytes": flush_bytes, "us": round(swp_ms / K * 1e3, 2),
+            "gbs": round(flush_bytes / (swp_ms / K * 1e-3) / 1e9, 1),
+            "kernel": "torch sum over a %d MiB fp32 tensor" % args.flush_mib}),
         "max_abs_err_vs_oracle_b0": None,
         "roofline": {
             "bound": "hbm",
