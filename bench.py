@@ -40,7 +40,8 @@ METRIC = "GQA decode attention µs/step + achieved KV-read HBM GB/s (% of peak)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_decode_amd", "csrc", f)
-                  for f in ("gqa_kernels.hip", "gqa_api.cpp", "gqa_internal.h", "gqa_chunkmap.h")]
+                  for f in ("gqa_kernels.hip", "gqa_api.cpp", "gqa_internal.h", "gqa_chunkmap.h")] + \
+    [os.path.join(ROOT, "grouped_query_attention_decode_amd", "build.py")]
 
 
 def log(*a):
