@@ -72,6 +72,27 @@ def test_random_decode(gqa, orc, i):
     assert _err(got, want) <= TOL[dt], c
 
 
+@pytest.mark.parametrize("forced", [("GQA_RSPLIT", "0"), ("GQA_RSPLIT", "2"), ("GQA_MFX", "0")],
+                         ids=["one_wave", "row_split_2", "no_32x32"])
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_decode_other_kernels(gqa, orc, monkeypatch, i, forced):
+    """The same shapes (bf16) with the planner's development switches forcing
+    the kernels the default plans do not pick for them: one-wave workgroups
+    instead of row-split ones on small caches, two-wave row splits, and the
+    16 x 16 kernels instead of the 32 x 32 one above 16 query rows."""
+    if i % 6 == 5:
+        pytest.skip("fp32 shapes run on the vector-ALU kernel only")
+    c = _shape(i)
+    monkeypatch.setenv(*forced)
+    x = gi.make_custom(c["B"], c["H"], c["G"], c["D"], c["T"], c["sq"], dtype="bf16", seed=c["seed"],
+                       seq_lens=c["lens"])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(c["D"]))
+    got = gqa.decode(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["seq_lens"].cuda(),
+                     workgroups=c["P"], merge=c["merge"])
+    torch.cuda.synchronize()
+    assert _err(got, want) <= TOL["bf16"], (c, forced)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_append(gqa, orc, i):
     c = _shape(i)
