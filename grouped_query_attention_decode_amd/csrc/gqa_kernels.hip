@@ -309,68 +309,149 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int lane)
     return x;
 }
 
+constexpr int kLensWindow = 256;   // seq_lens entries a wave keeps in LDS
+
 // ---------------------------------------------------------------------------
-// Equal-work schedule.  Work units: cache rows of all segments, segments in
-// order (b, g, row block).  Workgroup p owns units [start(p), start(p+1)).
+// Work split, the same for every kernel.  Work is counted in cost units: a
+// segment (sequence b, KV head g, row block rb) with L > 0 cache rows costs
+// piece_cost + L -- its rows plus what starting a piece of it costs a
+// workgroup (loading its queries, filling the load pipeline, writing its
+// result).  All segments end to end span V cost units, cut into P chunks
+// with fixed boundaries, chunk c = [c V / P, (c + 1) V / P), taken by
+// workgroup c; with V < P only the first V workgroups take one unit each.
+// A chunk that holds the start of a segment (so one more piece) thereby
+// gets fewer rows.  A piece is a chunk's part of one segment's rows; its
+// partial lives in a slot of the chunk, and merges go in chunk order.  A
+// chunk may hold only start cost and no rows: it has no piece, and no
+// segment counts it among its pieces (every chunk between a segment's first
+// and last row holds rows of it).
+//
+// (A guided deal -- most of each share static, the rest in small chunks
+// handed out by a global counter -- was measured slower on every workload:
+// thousands of device-scope atomics on one address serialise.)
 // ---------------------------------------------------------------------------
-// (Exact quotients by div_floor: no 64-bit integer division on the GPU.)
-__device__ __forceinline__ long long wg_start(long long W, int P, int p)
+// Cost units of one segment of a sequence with L clamped rows; pc: the
+// plan's charge for starting a piece (a.piece_cost).
+__device__ __forceinline__ uint32_t seg_cost(int L, int pc)
 {
-    return div_floor((long long)p * W, P, 1.0 / (double)P);
+    return L > 0 ? (uint32_t)(L + pc) : 0u;
 }
 
-// The workgroup whose range holds unit x (0 <= x < W).
-__device__ __forceinline__ int wg_of(long long x, long long W, int P)
-{
-    return (int)div_floor((x + 1) * P - 1, W, 1.0 / (double)W);
-}
-
-// This workgroup's share of the work; every lane holds the same values.
-struct Sched {
-    long long total;     // W
-    long long first_b;   // first sequence this workgroup touches
-    long long first_e;   // units before that sequence
-    int P;               // workgroups that share the work: min(grid, W), so none is empty
+// Partial slots: two per chunk (slot 0 for the segment holding the chunk's
+// first unit, slot 1 for the one that starts inside it and runs past its
+// end), each a.slot_rows rows of D values, then their log2-sum-exp.
+struct MSlots {
+    int stride;   // floats per slot
+    int lse;      // offset of the log2-sum-exp values in a slot
+    __device__ __forceinline__ int base(int c, int which) const { return (2 * c + which) * stride; }
 };
 
-// W = units_per_seq * sum_b clamp(L_b); then the first sequence whose units
-// reach past this workgroup's start.  Executed by all 64 lanes of the wave.
-__device__ __forceinline__ Sched schedule_wave(const Args& a, int units_per_seq, int P, int p)
+template <int D>
+__device__ __forceinline__ MSlots mslots(const Args& a)
+{
+    MSlots m;
+    m.lse = a.slot_rows * D;
+    m.stride = slot_floats(a.slot_rows, D);
+    return m;
+}
+
+__device__ __forceinline__ int lens_at(const Args& a, const int* lens, int b)
+{
+    return b < kLensWindow ? lens[b] : clamp_len(a.seq_lens, b, a.T);
+}
+
+// Cost units of one segment of every sequence, summed (every lane gets it).
+__device__ __forceinline__ long long total_cost(const Args& a, const int* lens)
 {
     const int lane = threadIdx.x & (kWave - 1);
     long long tot = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        const uint32_t L = b < a.B ? (uint32_t)clamp_len(a.seq_lens, b, a.T) : 0u;
-        tot += wave_sum_u32(L);
+        tot += wave_sum_u32(b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u);
     }
-    Sched s;
-    s.total = tot * units_per_seq;
-    s.first_b = a.B;
-    s.first_e = s.total;
-    // with fewer units than workgroups, the first W take one unit each (an
-    // empty workgroup inside a segment's range would never arrive)
-    if (s.total > 0 && s.total < P) P = (int)s.total;
-    s.P = P;
-    const long long A = wg_start(s.total, P, p);
+    return tot;
+}
+
+// First sequence whose cost units reach past unit x, and the units before it.
+__device__ __forceinline__ void locate(const Args& a, const int* lens, int units, long long x, int& first_b,
+                                       long long& first_v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
     long long carry = 0;
-    for (int b0 = 0; b0 < a.B && s.total > 0; b0 += kWave) {
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
-        const uint32_t L = b < a.B ? (uint32_t)clamp_len(a.seq_lens, b, a.T) : 0u;
-        const uint32_t incl = wave_incl_scan_u32(L, lane);
-        const long long end_b = (carry + incl) * units_per_seq;
-        const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && end_b > A);
-        const uint32_t chunk_total = __shfl(incl, kWave - 1);
+        const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(c, lane);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
         if (hit) {
             const int f = __builtin_ctzll(hit);
-            s.first_b = b0 + f;
-            s.first_e = (carry + __shfl(incl - L, f)) * units_per_seq;
-            break;
+            first_b = b0 + f;
+            first_v = (carry + __shfl(incl - c, f)) * units;
+            return;
         }
-        carry += chunk_total;
+        carry += __shfl(incl, kWave - 1);
     }
-    return s;
+    first_b = a.B;
+    first_v = carry * units;
 }
+
+// One piece: a run [ta, tb) of cache rows of segment (b, g, rb).
+struct Piece {
+    int b, g, rb, ta, tb, L;
+    long long off;       // cost-unit position of the segment's first row
+};
+
+// Yields the pieces of the chunk [vA, vE) (cost units) in order; a piece's
+// `off` is the cost-unit position of its segment's first row.
+struct CostPieceIter {
+    long long vA, vE, Vb;   // the chunk; cost units before sequence b
+    int b, k, units, n_rb;
+
+    __device__ __forceinline__ void init(long long vA_, long long vE_, int fb, long long fv, int G, int n_rb_)
+    {
+        vA = vA_;
+        vE = vE_;
+        Vb = fv;
+        b = fb;
+        k = -1;
+        n_rb = n_rb_;
+        units = G * n_rb_;
+    }
+
+    __device__ __forceinline__ bool next(const Args& a, const int* lens, Piece& pc)
+    {
+        while (b < a.B && Vb < vE) {
+            const int Lb = lens_at(a, lens, b);
+            if (Lb > 0) {
+                const int pcost = a.piece_cost;
+                const long long sc = (long long)Lb + pcost;
+                // first piece of this sequence in the chunk (exact; no 64-bit division)
+                if (k < 0) k = vA > Vb ? (int)div_floor(vA - Vb, sc, 1.0 / (double)sc) : 0;
+                while (k < units) {
+                    const long long vfirst = Vb + k * sc + pcost;
+                    if (vfirst - pcost >= vE) return false;
+                    const long long ta = vA > vfirst ? vA - vfirst : 0;
+                    const long long tb = vE - vfirst < Lb ? vE - vfirst : Lb;
+                    const int kk = k++;
+                    if (tb > ta) {
+                        pc.b = b;
+                        pc.g = kk / n_rb;
+                        pc.rb = kk % n_rb;
+                        pc.ta = (int)ta;
+                        pc.tb = (int)tb;
+                        pc.L = Lb;
+                        pc.off = vfirst;
+                        return true;
+                    }
+                }
+            }
+            Vb += (long long)units * seg_cost(Lb, a.piece_cost);
+            ++b;
+            k = -1;
+        }
+        return false;
+    }
+};
 
 // Partials cross workgroups that may run on different XCDs, whose L2 caches
 // are not coherent with each other.  They are written and read through a
@@ -427,19 +508,20 @@ struct Pending {
     int row0;         // first query row of the segment within its KV head
 };
 
-// Partial slot of workgroup q for the segment starting at unit off: slot 0
-// when the segment holds q's first unit, else slot 1 (the segment that runs
-// past q's last unit).  A slot is RB rows of D values (16-byte aligned) and
-// then RB log2-sum-exp values (at least 16 floats); offset in floats.
+// Partial slot of chunk q for the segment whose first row is cost unit off:
+// slot 0 when the segment holds q's first unit, else slot 1 (the segment
+// that runs past q's last unit).  A slot is RB rows of D values (16-byte
+// aligned) and then RB log2-sum-exp values (at least 16 floats); offset in
+// floats.
 template <int D, int RB>
-__device__ __forceinline__ int slot_base(int q, long long off, long long W, int P)
+__device__ __forceinline__ int slot_base(int q, long long off, const ChunkMap& cm)
 {
-    return (q * 2 + (wg_start(W, P, q) >= off ? 0 : 1)) * slot_floats(RB, D);
+    return (q * 2 + (cm.start(q) >= off ? 0 : 1)) * slot_floats(RB, D);
 }
 
 // The same for the pieces of one segment, q = p_first + k: only the first
-// workgroup can hold the segment in its second slot (tail1: it started
-// before the segment), so no division per piece.
+// chunk can hold the segment in its second slot (tail1: it starts before
+// the segment's first row), so no division per piece.
 template <int D, int RB>
 __device__ __forceinline__ int piece_slot(int p_first, int k, bool tail1)
 {
@@ -469,13 +551,13 @@ template <int D, int RB, int EPL, int NAK>
 __device__ __forceinline__ bool piece_output(const Args& a, const float* row_m, const float* row_l,
                                              const float* acc, int ubase, int doff, int64_t qrow0,
                                              int row0, int R, int n_rb, int b, int g, int rb,
-                                             long long off, int L, long long W, int P, int p,
+                                             long long off, int L, const ChunkMap& cm, int chunk,
                                              Pending* pd)
 {
-    const int p_first = wg_of(off, W, P);
-    const int npieces = wg_of(off + L - 1, W, P) - p_first + 1;
+    const int p_first = cm.of(off);
+    const int npieces = cm.of(off + L - 1) - p_first + 1;
     const __amdgpu_buffer_rsrc_t part = part_rsrc(a.part);
-    const int mine = slot_base<D, RB>(p, off, W, P);
+    const int mine = slot_base<D, RB>(chunk, off, cm);
     float val[NAK];
 #pragma unroll
     for (int m = 0; m < NAK; ++m) {
@@ -530,7 +612,7 @@ __device__ __forceinline__ bool piece_output(const Args& a, const float* row_m, 
 // (s_waitcnt 0), so that the last arrival sees every partial.
 template <int D, int RB, int EPL, int NAK>
 __device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& pd, int lane, int ubase,
-                                                 int doff, int R, long long W, int P)
+                                                 int doff, int R, const ChunkMap& cm)
 {
     constexpr int NR = NAK >= EPL ? NAK / EPL : 1;    // query rows among a lane's accumulators
     int old = 0;
@@ -550,7 +632,7 @@ __device__ __forceinline__ void arrive_and_merge(const Args& a, const Pending& p
     }
 #pragma unroll
     for (int m = 0; m < NAK; ++m) num[m] = 0.0f;
-    const bool tail1 = wg_start(W, P, pd.p_first) < pd.off;
+    const bool tail1 = cm.start(pd.p_first) < pd.off;
     for (int k0 = 0; k0 < pd.npieces; k0 += 4) {
         // the loads of four pieces are in flight together
         float lse[4][NR], ov[4][NAK];
@@ -603,13 +685,13 @@ template <int D, int RB, int EPL, int NAK>
 __device__ __forceinline__ void finish_piece(const Args& a, const float* row_m, const float* row_l,
                                              const float* acc, int lane, int ubase, int doff,
                                              int64_t qrow0, int row0, int R, int n_rb, int b, int g,
-                                             int rb, long long off, int L, long long W, int P, int p)
+                                             int rb, long long off, int L, const ChunkMap& cm, int chunk)
 {
     Pending pd;
     if (piece_output<D, RB, EPL, NAK>(a, row_m, row_l, acc, ubase, doff, qrow0, row0, R, n_rb, b, g, rb,
-                                      off, L, W, P, p, &pd)) {
+                                      off, L, cm, chunk, &pd)) {
         partials_stored_before_arrival();    // own partial stores complete at device scope
-        arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, ubase, doff, R, W, P);
+        arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, ubase, doff, R, cm);
     }
 }
 
@@ -653,6 +735,7 @@ struct ValuShared {
     float alpha[RB];                   // per-row rescale factors
     float row_m[RB];                   // per-row max and sum at the end of a piece
     float row_l[RB];
+    int lens[kLensWindow];             // clamped seq_lens[i]
 };
 
 // Rows of sequences with no valid cache rows are all zeros; workgroup p
@@ -668,42 +751,14 @@ __device__ void zero_empty_sequences(const Args& a, int P, int p)
     }
 }
 
-// Walk this workgroup's pieces: fn(b, g, rb, ta, tb, off, Lb) for each.
-template <class Fn>
-__device__ __forceinline__ void for_each_piece(const Args& a, const Sched& sh, int n_rb, int P, int p,
-                                               Fn&& fn)
-{
-    const long long W = sh.total;
-    const long long A = wg_start(W, P, p);
-    const long long E = wg_start(W, P, p + 1);
-    if (A >= E) return;                      // more workgroups than units: nothing here
-    const int units = a.G * n_rb;
-    int b = (int)sh.first_b;
-    long long Eb = sh.first_e;
-    while (b < a.B && Eb < E) {
-        const int Lb = clamp_len(a.seq_lens, b, a.T);
-        if (Lb > 0) {
-            for (long long k = A > Eb ? (A - Eb) / Lb : 0; k < units; ++k) {
-                const long long off = Eb + k * Lb;
-                if (off >= E) break;
-                const int ta = (int)(A > off ? A - off : 0);
-                const int tb = (int)(E - off < Lb ? E - off : Lb);
-                fn(b, (int)(k / n_rb), (int)(k % n_rb), ta, tb, off, Lb);
-            }
-        }
-        Eb += (long long)units * Lb;
-        ++b;
-    }
-}
-
 // Stream cache rows [ta, tb) of segment (b, g, rb) -- one piece -- and
-// finish it: write out directly when the segment lies in this workgroup,
-// else leave a partial and merge all partials if this workgroup arrives last.
+// finish it: write out directly when the segment lies in this chunk, else
+// leave a partial and merge all partials if this piece arrives last.
 template <class FMT, int D, int RB>
 __device__ __forceinline__ void valu_piece(const Args& a, ValuShared<FMT, D, RB>& sm, int R, int n_rb,
-                                           int b, int g, int rb, int ta, int tb, long long off, int L,
-                                           long long W, int P, int p)
+                                           const Piece& pc, const ChunkMap& cm, int chunk)
 {
+    const int b = pc.b, g = pc.g, rb = pc.rb, ta = pc.ta, tb = pc.tb, L = pc.L;
     using Gm = ValuGeom<FMT, D, RB>;
     constexpr int ES = Gm::ES, EPL = Gm::EPL, LPT = Gm::LPT, TPL = Gm::TPL, NL = Gm::NL;
     constexpr int TW = Gm::TW, NV = Gm::NV, NSC = Gm::NSC, REP = Gm::REP;
@@ -872,7 +927,7 @@ __device__ __forceinline__ void valu_piece(const Args& a, ValuShared<FMT, D, RB>
     wave_lds_fence();
 
     finish_piece<D, RB, EPL, NAK>(a, sm.row_m, sm.row_l, acc, lane, lrow * NAK, doff, qrow0, row0, R,
-                                  n_rb, b, g, rb, off, L, W, P, p);
+                                  n_rb, b, g, rb, pc.off, L, cm, chunk);
     wave_lds_fence();   // row_m/row_l/pbuf are rewritten by the next piece
 }
 
@@ -881,16 +936,26 @@ __global__ void __launch_bounds__(kWave)
 decode_valu(const Args a, const int R, const int n_rb)
 {
     __shared__ ValuShared<FMT, D, RB> sm;
+    const int P = gridDim.x;
     const int p = blockIdx.x;
-    const Sched sched = schedule_wave(a, a.G * n_rb, gridDim.x, p);
-    zero_empty_sequences<D>(a, gridDim.x, p);
-    const int P = sched.P;
-    const long long W = sched.total;
-    if (W == 0) return;
-    for_each_piece(a, sched, n_rb, P, p,
-                   [&](int b, int g, int rb, int ta, int tb, long long off, int Lb) {
-                       valu_piece<FMT, D, RB>(a, sm, R, n_rb, b, g, rb, ta, tb, off, Lb, W, P, p);
-                   });
+    const int lane = threadIdx.x & (kWave - 1);
+    zero_empty_sequences<D>(a, P, p);
+    for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
+    wave_lds_fence();
+    const int units = a.G * n_rb;
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
+    int fb;
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
+    Piece pc;
+    while (it.next(a, sm.lens, pc)) valu_piece<FMT, D, RB>(a, sm, R, n_rb, pc, cm, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -908,13 +973,12 @@ decode_valu(const Args a, const int R, const int n_rb)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kLensWindow = 256;   // seq_lens entries a wave keeps in LDS
 
 struct MqkShared {
     float pbuf[16][16];      // p of the current tile: [cache row][query row]
     float row_m[16];         // per-row max and sum at the end of a piece
     float row_l[16];
-    int lens[kLensWindow];   // clamped seq_lens[first_b + i]
+    int lens[kLensWindow];   // clamped seq_lens[i]
 };
 
 template <int M>
@@ -941,80 +1005,12 @@ __device__ __forceinline__ float readlane_f(float x, int l)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// One piece: a run [ta, tb) of cache rows of segment (b, g, rb).
-struct Piece {
-    int b, g, rb, ta, tb, L;
-    long long off;       // the segment's first work unit
-};
-
-// Yields this workgroup's pieces in order (the same walk as for_each_piece).
-struct PieceIter {
-    long long A, E, Eb, k;
-    int b, units, n_rb;
-
-    // the units [A_, E_) of one chunk; fb / fe: first sequence reaching past
-    // A_ and the units before it
-    __device__ __forceinline__ void init_range(long long A_, long long E_, int fb, long long fe, int G,
-                                               int n_rb_)
-    {
-        A = A_;
-        E = E_;
-        Eb = fe;
-        b = fb;
-        k = -1;
-        n_rb = n_rb_;
-        units = G * n_rb_;
-    }
-
-    __device__ __forceinline__ void init(const Sched& sh, int G, int n_rb_, int P, int p)
-    {
-        A = wg_start(sh.total, P, p);
-        E = wg_start(sh.total, P, p + 1);
-        Eb = sh.first_e;
-        b = (int)sh.first_b;
-        k = -1;
-        n_rb = n_rb_;
-        units = G * n_rb_;
-    }
-
-    // lens: LDS copy of the clamped seq_lens from first_b on (kLensWindow of
-    // them): the walk runs inside the tile stream, where a global load would
-    // make the wave wait for every tile load in flight.
-    __device__ __forceinline__ bool next(const Args& a, const int* lens, int base, Piece& pc)
-    {
-        while (b < a.B && Eb < E) {
-            const int Lb = (b - base < kLensWindow) ? lens[b - base] : clamp_len(a.seq_lens, b, a.T);
-            if (Lb > 0) {
-                if (k < 0) k = A > Eb ? (A - Eb) / Lb : 0;
-                if (k < units) {
-                    const long long off = Eb + k * Lb;
-                    if (off < E) {
-                        pc.b = b;
-                        pc.g = (int)(k / n_rb);
-                        pc.rb = (int)(k % n_rb);
-                        pc.ta = (int)(A > off ? A - off : 0);
-                        pc.tb = (int)(E - off < Lb ? E - off : Lb);
-                        pc.L = Lb;
-                        pc.off = off;
-                        ++k;
-                        return true;
-                    }
-                }
-            }
-            Eb += (long long)units * Lb;
-            ++b;
-            k = -1;
-        }
-        return false;
-    }
-};
-
 // One piece of segment (b, g, rb): cache rows [ta, tb).  The wave streams
 // 16-row tiles with the loads of the next two tiles in flight, then writes
 // the piece out (or stores its partial, returned in *pd without waiting).
 template <int D, int RB>
 __device__ __forceinline__ bool mqk_piece(const Args& a, MqkShared& sm, int R, int n_rb, const Piece& pc,
-                                          long long W, int P, int p, Pending* pd)
+                                          const ChunkMap& cm, int chunk, Pending* pd)
 {
     constexpr int NK = D / 32;           // matrix-core k steps per tile
     constexpr int EPL = 8;               // bf16 per 16-byte load (V layout)
@@ -1171,7 +1167,7 @@ __device__ __forceinline__ bool mqk_piece(const Args& a, MqkShared& sm, int R, i
     }
     wave_lds_fence();
     const bool left = piece_output<D, RB, EPL, NAK>(a, sm.row_m, sm.row_l, acc, lrow * NAK, doff, qrow0, row0,
-                                                    R, n_rb, pc.b, pc.g, pc.rb, pc.off, pc.L, W, P, p, pd);
+                                                    R, n_rb, pc.b, pc.g, pc.rb, pc.off, pc.L, cm, chunk, pd);
     wave_lds_fence();   // row_m / row_l / pbuf are rewritten by the next piece
     return left;
 }
@@ -1187,26 +1183,30 @@ decode_mqk(const Args a, const int R, const int n_rb)
     constexpr int LPT = D / EPL;
     constexpr int NAK = RB * EPL / (kWave / LPT);
     __shared__ MqkShared sm;
+    const int P = gridDim.x;
     const int p = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
-    const Sched sched = schedule_wave(a, a.G * n_rb, gridDim.x, p);
-    zero_empty_sequences<D>(a, gridDim.x, p);
-    const int P = sched.P;
-    const long long W = sched.total;
-    if (W == 0) return;
-    const int lbase = (int)sched.first_b;
-    for (int i = lane; i < kLensWindow; i += kWave)
-        sm.lens[i] = lbase + i < a.B ? clamp_len(a.seq_lens, lbase + i, a.T) : 0;
+    zero_empty_sequences<D>(a, P, p);
+    for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
-
-    PieceIter it;
-    it.init(sched, a.G, n_rb, P, p);
+    const int units = a.G * n_rb;
+    const long long V = total_cost(a, sm.lens) * units;
+    if (V == 0) return;
+    const ChunkMap cm = make_map(V, P);
+    const int chunk = p;
+    if (chunk >= cm.P) return;               // fewer cost units than workgroups
+    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
+    int fb;
+    long long fv;
+    locate(a, sm.lens, units, vA, fb, fv);
+    CostPieceIter it;
+    it.init(vA, vE, fb, fv, a.G, n_rb);
     Piece pc;
-    while (it.next(a, sm.lens, lbase, pc)) {
+    while (it.next(a, sm.lens, pc)) {
         Pending pd;
-        if (mqk_piece<D, RB>(a, sm, R, n_rb, pc, W, P, p, &pd)) {
+        if (mqk_piece<D, RB>(a, sm, R, n_rb, pc, cm, chunk, &pd)) {
             partials_stored_before_arrival();    // own partial stores complete at device scope
-            arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, (lane / LPT) * NAK, (lane % LPT) * EPL, R, W, P);
+            arrive_and_merge<D, RB, EPL, NAK>(a, pd, lane, (lane / LPT) * NAK, (lane % LPT) * EPL, R, cm);
         }
     }
 }
@@ -1365,143 +1365,6 @@ __device__ __forceinline__ float sum_x32(float x)
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// ---------------------------------------------------------------------------
-// Work split of the matrix-core pass.  Work is counted in cost units: a
-// segment (sequence b, KV head g, row block rb) with L > 0 cache rows costs
-// piece_cost + L -- its rows plus what starting a piece of it costs a
-// workgroup (loading its queries, filling the load pipeline, writing its
-// result).  All segments end to end span V cost units, cut into P chunks
-// with fixed boundaries, chunk c = [c V / P, (c + 1) V / P), taken by
-// workgroup c; with V < P only the first V workgroups take one unit each.
-// A chunk that holds the start of a segment (so one more piece) thereby
-// gets fewer rows.  A piece is a chunk's part of one segment's rows; its
-// partial lives in a slot of the chunk, and merges go in chunk order.  A
-// chunk may hold only start cost and no rows: it has no piece, and no
-// segment counts it among its pieces (every chunk between a segment's first
-// and last row holds rows of it).
-//
-// (A guided deal -- most of each share static, the rest in small chunks
-// handed out by a global counter -- was measured slower on every workload:
-// thousands of device-scope atomics on one address serialise.)
-// ---------------------------------------------------------------------------
-// Cost units of one segment of a sequence with L clamped rows; pc: the
-// plan's charge for starting a piece (a.piece_cost).
-__device__ __forceinline__ uint32_t seg_cost(int L, int pc)
-{
-    return L > 0 ? (uint32_t)(L + pc) : 0u;
-}
-
-// Partial slots of the matrix-core pass: two per chunk (slot 0 for the
-// segment holding the chunk's first unit, slot 1 for the one that starts
-// inside it and runs past its end), each a.slot_rows rows of D values, then
-// their log2-sum-exp.
-struct MSlots {
-    int stride;   // floats per slot
-    int lse;      // offset of the log2-sum-exp values in a slot
-    __device__ __forceinline__ int base(int c, int which) const { return (2 * c + which) * stride; }
-};
-
-template <int D>
-__device__ __forceinline__ MSlots mslots(const Args& a)
-{
-    MSlots m;
-    m.lse = a.slot_rows * D;
-    m.stride = slot_floats(a.slot_rows, D);
-    return m;
-}
-
-__device__ __forceinline__ int lens_at(const Args& a, const int* lens, int b)
-{
-    return b < kLensWindow ? lens[b] : clamp_len(a.seq_lens, b, a.T);
-}
-
-// Cost units of one segment of every sequence, summed (every lane gets it).
-__device__ __forceinline__ long long total_cost(const Args& a, const int* lens)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    long long tot = 0;
-    for (int b0 = 0; b0 < a.B; b0 += kWave) {
-        const int b = b0 + lane;
-        tot += wave_sum_u32(b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u);
-    }
-    return tot;
-}
-
-// First sequence whose cost units reach past unit x, and the units before it.
-__device__ __forceinline__ void locate(const Args& a, const int* lens, int units, long long x, int& first_b,
-                                       long long& first_v)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    long long carry = 0;
-    for (int b0 = 0; b0 < a.B; b0 += kWave) {
-        const int b = b0 + lane;
-        const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u;
-        const uint32_t incl = wave_incl_scan_u32(c, lane);
-        const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
-        if (hit) {
-            const int f = __builtin_ctzll(hit);
-            first_b = b0 + f;
-            first_v = (carry + __shfl(incl - c, f)) * units;
-            return;
-        }
-        carry += __shfl(incl, kWave - 1);
-    }
-    first_b = a.B;
-    first_v = carry * units;
-}
-
-// Yields the pieces of the chunk [vA, vE) (cost units) in order; a piece's
-// `off` is the cost-unit position of its segment's first row.
-struct CostPieceIter {
-    long long vA, vE, Vb;   // the chunk; cost units before sequence b
-    int b, k, units, n_rb;
-
-    __device__ __forceinline__ void init(long long vA_, long long vE_, int fb, long long fv, int G, int n_rb_)
-    {
-        vA = vA_;
-        vE = vE_;
-        Vb = fv;
-        b = fb;
-        k = -1;
-        n_rb = n_rb_;
-        units = G * n_rb_;
-    }
-
-    __device__ __forceinline__ bool next(const Args& a, const int* lens, Piece& pc)
-    {
-        while (b < a.B && Vb < vE) {
-            const int Lb = lens_at(a, lens, b);
-            if (Lb > 0) {
-                const int pcost = a.piece_cost;
-                const long long sc = (long long)Lb + pcost;
-                // first piece of this sequence in the chunk (exact; no 64-bit division)
-                if (k < 0) k = vA > Vb ? (int)div_floor(vA - Vb, sc, 1.0 / (double)sc) : 0;
-                while (k < units) {
-                    const long long vfirst = Vb + k * sc + pcost;
-                    if (vfirst - pcost >= vE) return false;
-                    const long long ta = vA > vfirst ? vA - vfirst : 0;
-                    const long long tb = vE - vfirst < Lb ? vE - vfirst : Lb;
-                    const int kk = k++;
-                    if (tb > ta) {
-                        pc.b = b;
-                        pc.g = kk / n_rb;
-                        pc.rb = kk % n_rb;
-                        pc.ta = (int)ta;
-                        pc.tb = (int)tb;
-                        pc.L = Lb;
-                        pc.off = vfirst;
-                        return true;
-                    }
-                }
-            }
-            Vb += (long long)units * seg_cost(Lb, a.piece_cost);
-            ++b;
-            k = -1;
-        }
-        return false;
-    }
-};
 
 // One piece of segment (b, g, rb) -- cache rows [ta, tb) for the RB = 16 NB
 // query rows RB rb .. RB rb + RB - 1 -- streamed in 32-row tiles with the
