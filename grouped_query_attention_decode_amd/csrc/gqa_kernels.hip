@@ -299,14 +299,27 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x)
     return x;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int lane)
+// Inclusive prefix sum over the wave, on DPP moves only (no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with
+// no source read 0), then row_bcast:15 adds the last lane of rows 0 and 2
+// to rows 1 and 3, and row_bcast:31 the last lane of row 1 (the sum of rows
+// 0 and 1) to rows 2 and 3.  Rows the row mask leaves out add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    return x;
+    int v = (int)x;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return (uint32_t)v;
+}
+
+// x of lane l (l uniform across the wave), without an LDS round trip.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t x, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
 }
 
 constexpr int kLensWindow = 256;   // seq_lens entries a wave keeps in LDS
@@ -381,18 +394,61 @@ __device__ __forceinline__ void locate(const Args& a, const int* lens, int units
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
         const int b = b0 + lane;
         const uint32_t c = b < a.B ? seg_cost(lens_at(a, lens, b), a.piece_cost) : 0u;
-        const uint32_t incl = wave_incl_scan_u32(c, lane);
+        const uint32_t incl = wave_incl_scan_u32(c);
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(b < a.B && (carry + incl) * units > x);
         if (hit) {
             const int f = __builtin_ctzll(hit);
             first_b = b0 + f;
-            first_v = (carry + __shfl(incl - c, f)) * units;
+            first_v = (carry + lane_u32(incl - c, f)) * units;
             return;
         }
-        carry += __shfl(incl, kWave - 1);
+        carry += lane_u32(incl, kWave - 1);
     }
     first_b = a.B;
     first_v = carry * units;
+}
+
+// This workgroup's chunk of the split: the chunk map, the chunk [vA, vE) in
+// cost units, the first sequence whose units reach past vA and the units
+// before it.
+struct ChunkPlan {
+    ChunkMap cm;
+    long long vA, vE, fv;
+    int fb;
+};
+
+// Plans chunk `chunk` of P; false when it holds no work (no cost units at
+// all, or fewer units than workgroups and this chunk past them).  Up to 64
+// sequences take one pass: the scan of the segment costs gives the total
+// (its last lane) and, by a ballot, the first sequence past vA.
+__device__ __forceinline__ bool plan_chunk(const Args& a, const int* lens, int units, int P, int chunk,
+                                           ChunkPlan& cp)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (a.B <= kWave) {
+        const uint32_t c = lane < a.B ? seg_cost(lens[lane], a.piece_cost) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(c);
+        const long long V = (long long)lane_u32(incl, kWave - 1) * units;
+        if (V == 0) return false;
+        cp.cm = make_map(V, P);
+        if (chunk >= cp.cm.P) return false;
+        cp.vA = cp.cm.start(chunk);
+        cp.vE = cp.cm.start(chunk + 1);
+        // some lane below B reaches past vA < V
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < a.B && (long long)incl * units > cp.vA);
+        const int f = __builtin_ctzll(hit);
+        cp.fb = f;
+        cp.fv = (long long)(lane_u32(incl, f) - lane_u32(c, f)) * units;
+        return true;
+    }
+    const long long V = total_cost(a, lens) * units;
+    if (V == 0) return false;
+    cp.cm = make_map(V, P);
+    if (chunk >= cp.cm.P) return false;
+    cp.vA = cp.cm.start(chunk);
+    cp.vE = cp.cm.start(chunk + 1);
+    locate(a, lens, units, cp.vA, cp.fb, cp.fv);
+    return true;
 }
 
 // One piece: a run [ta, tb) of cache rows of segment (b, g, rb).
@@ -943,17 +999,12 @@ decode_valu(const Args a, const int R, const int n_rb)
     for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) valu_piece<FMT, D, RB>(a, sm, R, n_rb, pc, cm, chunk);
 }
@@ -1190,17 +1241,12 @@ decode_mqk(const Args a, const int R, const int n_rb)
     for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
@@ -1888,17 +1934,12 @@ decode_mfa(const Args a, const int R, const int n_rb)
     for (int i = lane; i < kLensWindow && i < a.B; i += kWave) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     wave_lds_fence();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
@@ -1927,17 +1968,12 @@ decode_mfs(const Args a, const int R, const int n_rb)
     for (int i = threadIdx.x; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     __syncthreads();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
@@ -2199,17 +2235,12 @@ decode_mfw(const Args a, const int R, const int n_rb)
     for (int i = tid; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     __syncthreads();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
@@ -2728,17 +2759,12 @@ decode_mfx(const Args a, const int R, const int n_rb)
     for (int i = tid; i < kLensWindow && i < a.B; i += kWave * NW) sm.lens[i] = clamp_len(a.seq_lens, i, a.T);
     __syncthreads();
     const int units = a.G * n_rb;
-    const long long V = total_cost(a, sm.lens) * units;
-    if (V == 0) return;
-    const ChunkMap cm = make_map(V, P);
     const int chunk = p;
-    if (chunk >= cm.P) return;               // fewer cost units than workgroups
-    const long long vA = cm.start(chunk), vE = cm.start(chunk + 1);
-    int fb;
-    long long fv;
-    locate(a, sm.lens, units, vA, fb, fv);
+    ChunkPlan cp;
+    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    const ChunkMap& cm = cp.cm;
     CostPieceIter it;
-    it.init(vA, vE, fb, fv, a.G, n_rb);
+    it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;

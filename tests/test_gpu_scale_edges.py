@@ -55,6 +55,25 @@ def test_more_sequences_than_the_lds_length_window(gqa, orc):
     assert _err(got, want) <= TOL
 
 
+@pytest.mark.parametrize("B", [63, 64, 65, 129])
+def test_batch_sizes_around_one_wave_of_sequences(gqa, orc, B):
+    """Up to 64 sequences the split is planned in one pass over the wave (one
+    sequence per lane); more take the loop over 64-sequence windows.  Ragged
+    lengths with empty sequences, on every kernel family."""
+    T = 80
+    lens = [int(x) for x in np.random.default_rng(B).integers(0, T + 1, size=B)]
+    lens[0], lens[-1] = 0, T
+    for (H, G, dt, kw) in [(8, 2, "bf16", {}),                       # 4 rows: one-wave / row-split kernel
+                           (8, 2, "bf16", {"path": gqa.PATH_MFMA_QK}),
+                           (8, 2, "f32", {}),                        # vector-ALU kernel
+                           (32, 1, "bf16", {})]:                     # 32 rows: 32 x 32 kernel
+        x = gi.make_custom(B, H, G, 64, T, 1, dtype=dt, seed=710 + B, seq_lens=lens)
+        want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], threads=8)
+        got = gqa.decode(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["seq_lens"].cuda(), **kw)
+        torch.cuda.synchronize()
+        assert _err(got, want) <= (TOL if dt == "bf16" else 1e-5), (H, G, dt, kw)
+
+
 def test_one_long_sequence(gqa, orc):
     """131072 cache rows in one (sequence, KV head): every workgroup holds a
     piece of the same two segments."""
