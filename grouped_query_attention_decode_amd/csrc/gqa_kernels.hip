@@ -322,6 +322,21 @@ __device__ __forceinline__ uint32_t lane_u32(uint32_t x, int l)
     return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
 }
 
+// A value every lane of the wave holds, marked as such for the compiler
+// (read from the first active lane), so that what is computed from it lives
+// in scalar registers and branches on it are scalar branches.
+__device__ __forceinline__ long long uniform_i64(long long x)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)x);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double uniform_f64(double x)
+{
+    return __builtin_bit_cast(double, uniform_i64(__builtin_bit_cast(long long, x)));
+}
+
 constexpr int kLensWindow = 256;   // seq_lens entries a wave keeps in LDS
 
 // ---------------------------------------------------------------------------
@@ -421,6 +436,11 @@ struct ChunkPlan {
 // all, or fewer units than workgroups and this chunk past them).  Up to 64
 // sequences take one pass: the scan of the segment costs gives the total
 // (its last lane) and, by a ballot, the first sequence past vA.
+// SCALAR: mark the plan wave-uniform (readfirstlane), so that the piece walk
+// built on it runs on scalar registers and branches.  Kernels short of
+// scalar registers keep the per-lane form: with it the 32 x 32 kernel
+// spilled scalars to vector lanes (64 new tokens 61.75 -> 64.43 us).
+template <bool SCALAR>
 __device__ __forceinline__ bool plan_chunk(const Args& a, const int* lens, int units, int P, int chunk,
                                            ChunkPlan& cp)
 {
@@ -432,8 +452,16 @@ __device__ __forceinline__ bool plan_chunk(const Args& a, const int* lens, int u
         if (V == 0) return false;
         cp.cm = make_map(V, P);
         if (chunk >= cp.cm.P) return false;
+        if constexpr (SCALAR) {
+            cp.cm.rV = uniform_f64(cp.cm.rV);
+            cp.cm.rP = uniform_f64(cp.cm.rP);
+        }
         cp.vA = cp.cm.start(chunk);
         cp.vE = cp.cm.start(chunk + 1);
+        if constexpr (SCALAR) {
+            cp.vA = uniform_i64(cp.vA);
+            cp.vE = uniform_i64(cp.vE);
+        }
         // some lane below B reaches past vA < V
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < a.B && (long long)incl * units > cp.vA);
         const int f = __builtin_ctzll(hit);
@@ -441,13 +469,22 @@ __device__ __forceinline__ bool plan_chunk(const Args& a, const int* lens, int u
         cp.fv = (long long)(lane_u32(incl, f) - lane_u32(c, f)) * units;
         return true;
     }
-    const long long V = total_cost(a, lens) * units;
+    long long V = total_cost(a, lens) * units;
+    if constexpr (SCALAR) V = uniform_i64(V);
     if (V == 0) return false;
     cp.cm = make_map(V, P);
     if (chunk >= cp.cm.P) return false;
     cp.vA = cp.cm.start(chunk);
     cp.vE = cp.cm.start(chunk + 1);
     locate(a, lens, units, cp.vA, cp.fb, cp.fv);
+    if constexpr (SCALAR) {
+        cp.cm.rV = uniform_f64(cp.cm.rV);
+        cp.cm.rP = uniform_f64(cp.cm.rP);
+        cp.vA = uniform_i64(cp.vA);
+        cp.vE = uniform_i64(cp.vE);
+        cp.fb = __builtin_amdgcn_readfirstlane(cp.fb);
+        cp.fv = uniform_i64(cp.fv);
+    }
     return true;
 }
 
@@ -459,6 +496,7 @@ struct Piece {
 
 // Yields the pieces of the chunk [vA, vE) (cost units) in order; a piece's
 // `off` is the cost-unit position of its segment's first row.
+template <bool SCALAR>
 struct CostPieceIter {
     long long vA, vE, Vb;   // the chunk; cost units before sequence b
     int b, k, units, n_rb;
@@ -477,7 +515,12 @@ struct CostPieceIter {
     __device__ __forceinline__ bool next(const Args& a, const int* lens, Piece& pc)
     {
         while (b < a.B && Vb < vE) {
-            const int Lb = lens_at(a, lens, b);
+            // every lane reads the same length; SCALAR: readfirstlane tells
+            // the compiler so, and the walk runs on scalar registers and
+            // branches (as a per-lane value, on the vector ALU under exec
+            // masks: ~0.5 us per piece with one wave per SIMD)
+            int Lb = lens_at(a, lens, b);
+            if constexpr (SCALAR) Lb = __builtin_amdgcn_readfirstlane(Lb);
             if (Lb > 0) {
                 const int pcost = a.piece_cost;
                 const long long sc = (long long)Lb + pcost;
@@ -1001,9 +1044,9 @@ decode_valu(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<false>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<false> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) valu_piece<FMT, D, RB>(a, sm, R, n_rb, pc, cm, chunk);
@@ -1243,9 +1286,9 @@ decode_mqk(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<false>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<false> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
@@ -1926,6 +1969,11 @@ template <int D, int NB, int SRC, bool KV8>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const Args a, const int R, const int n_rb)
 {
+    // the piece walk on scalar registers for the plain bf16 cache with one
+    // query block (batched GQA-8 decode 61.75 -> 60.79 us, the sq = 2 sweep
+    // at G = 8 158.7 -> 157.5); the other variants run out of scalar
+    // registers with it (spills to vector lanes; appended tokens 60.9 -> 61.8)
+    constexpr bool kScalarWalk = SRC == kSrcCache && !KV8 && NB == 1;
     __shared__ MfaShared<D> sm;
     const int P = gridDim.x;
     const int p = blockIdx.x;
@@ -1936,9 +1984,9 @@ decode_mfa(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<kScalarWalk>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<kScalarWalk> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
@@ -1970,9 +2018,9 @@ decode_mfs(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<false>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<false> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
@@ -2237,9 +2285,9 @@ decode_mfw(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<false>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<false> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
@@ -2761,9 +2809,9 @@ decode_mfx(const Args a, const int R, const int n_rb)
     const int units = a.G * n_rb;
     const int chunk = p;
     ChunkPlan cp;
-    if (!plan_chunk(a, sm.lens, units, P, chunk, cp)) return;
+    if (!plan_chunk<false>(a, sm.lens, units, P, chunk, cp)) return;
     const ChunkMap& cm = cp.cm;
-    CostPieceIter it;
+    CostPieceIter<false> it;
     it.init(cp.vA, cp.vE, cp.fb, cp.fv, a.G, n_rb);
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
