@@ -1062,7 +1062,7 @@ decode_valu(const Args a, const int R, const int n_rb)
 //   result:          lane l holds S[4*(l/16) + jj][l % 16], jj = 0..3
 // A and B give every lane's k slots the same head-dim elements, so the
 // products pair up correctly whatever order the unit sums them in.  Rows of
-// the block past RB (or past R) are zero in A and masked in S.
+// the block past RB (or past R) repeat its first row in A and are masked in S.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -1125,16 +1125,14 @@ __device__ __forceinline__ bool mqk_piece(const Args& a, MqkShared& sm, int R, i
     const int row0 = pc.rb * RB;
     const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
 
-    // A operand: query row `col` of the block (zero past RB or R)
+    // A operand: query row `col` of the block; rows past RB or R read the
+    // block's first row (their scores are masked, and never stored)
     uint4 qa[NK];
     {
         const bool live = col < RB && row0 + col < R;
         const char* qp = static_cast<const char*>(a.q) + ((qrow0 + (live ? col : 0)) * D + 8 * kg) * 2;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            const uint4 v = load16(qp + 64 * s);
-            qa[s] = live ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < NK; ++s) qa[s] = load16(qp + 64 * s);
     }
     int last[4];
     float m_run[4], l_run[4];
@@ -1493,7 +1491,11 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
     const int row0 = pc.rb * RB;
     const int64_t qrow0 = (int64_t)pc.b * a.H * a.sq + (int64_t)pc.g * R + row0;
 
-    // B operands of the score product: query row 16 nb + col, zero past R
+    // B operands of the score product: query row 16 nb + col.  Rows past R
+    // read the block's first row: their scores are masked (last = -1) or, in a
+    // full tile, feed only their own rows, which are never stored; no select
+    // on the loaded values, so nothing waits for these loads before the first
+    // tile's compute.
     uint4 qb[NB][NK];
     bool live[NB];
     int last[NB];
@@ -1507,10 +1509,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
         l_run[nb] = 0.0f;
         const char* qp = static_cast<const char*>(a.q) + (qrow0 + (live[nb] ? 16 * nb + col : 0)) * D * 2;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            const uint4 v = load16(qp + 2 * kdim0<D, KV8>(kg, s));
-            qb[nb][s] = live[nb] ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < NK; ++s) qb[nb][s] = load16(qp + 2 * kdim0<D, KV8>(kg, s));
     }
     f32x4_t acc[NB][NC];
 #pragma unroll
@@ -2085,10 +2084,7 @@ __device__ __forceinline__ bool mfw_piece(const Args& a, MfwShared<D, NW>& sm, i
     {
         const char* qp = static_cast<const char*>(a.q) + (qrow0 + (live ? 16 * w + col : 0)) * D * 2;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            const uint4 v = load16(qp + 2 * kdim0<D, false>(kg, s));
-            qb[s] = live ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < NK; ++s) qb[s] = load16(qp + 2 * kdim0<D, false>(kg, s));
     }
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4_t acc[NC];
