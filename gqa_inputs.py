@@ -41,13 +41,13 @@ class Workload:
     D: int
     T: int
     sq: int
-    dtype: str          # "f32" (q/k/v fp32) or "bf16" (q/k/v bf16); out is fp32
+    dtype: str          # "f32", "bf16" or "f16": the type of q, k and v; out is fp32
     seed: int
     ragged: Optional[Tuple[int, int]] = None   # inclusive (lo, hi) for seq_lens
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
     @property
     def elem_bytes(self) -> int:

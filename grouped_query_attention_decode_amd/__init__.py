@@ -7,8 +7,8 @@ missing or fails to load, every call raises -- there is no fallback.
 
     out = decode(q, k_cache, v_cache, seq_lens=None, scale=None, out=None)
 
-q [B,H,sq,D], k_cache / v_cache [B,G,T,D] (contiguous, on one GPU, both
-float32 or both bfloat16), seq_lens [B] int32 on the same GPU or None,
+q [B,H,sq,D], k_cache / v_cache [B,G,T,D] (contiguous, on one GPU, all
+float32, all bfloat16 or all float16), seq_lens [B] int32 on the same GPU or None,
 out [B,H,sq,D] float32.  Query head h reads KV head h // (H/G)
 ("GQA (Grouped-Query Attention) 분석", section "Grouped broadcast").
 
@@ -37,7 +37,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
-GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_F16 = 0, 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
 MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
@@ -156,6 +156,8 @@ def _dtype_code(dt) -> int:
         return GQA_F32
     if dt == torch.bfloat16:
         return GQA_BF16
+    if dt == torch.float16:
+        return GQA_F16
     if dt in (torch.uint8, torch.float8_e4m3fn):
         return GQA_FP8_E4M3
     return 99  # rejected by the library as unsupported

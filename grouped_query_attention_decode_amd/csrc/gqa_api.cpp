@@ -71,10 +71,13 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     const bool f32 = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32 && s->out_dtype == GQA_F32;
     const bool fp8 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_FP8_E4M3 && s->out_dtype == GQA_F32;
     const bool bf16 = (s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_BF16 && s->out_dtype == GQA_F32) || fp8;
-    if (!f32 && !bf16)
+    const bool f16 = s->q_dtype == GQA_F16 && s->kv_dtype == GQA_F16 && s->out_dtype == GQA_F32;
+    if (!f32 && !bf16 && !f16)
         return fail(GQA_ERR_UNSUPPORTED,
-                    "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32), (BF16,BF16,F32) or "
-                    "(BF16,FP8_E4M3,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
+                    "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32), (BF16,BF16,F32), "
+                    "(F16,F16,F32) or (BF16,FP8_E4M3,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
+    if (f16 && src != 0)
+        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need a bf16 cache");
     if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
         return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
     if ((int64_t)s->B * s->H * s->sq * s->D >= (int64_t)1 << 40)
@@ -94,15 +97,17 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
             return fail(GQA_ERR_INVALID_ARG, "unknown path %d", path_req);
         if (wg_req < 0) return fail(GQA_ERR_INVALID_ARG, "workgroups must be >= 0");
     }
-    if ((path_req == GQA_PATH_MFMA || path_req == GQA_PATH_MFMA_QK) && !bf16)
-        return fail(GQA_ERR_UNSUPPORTED, "the matrix-core paths need bf16 q/k/v");
+    if ((path_req == GQA_PATH_MFMA || path_req == GQA_PATH_MFMA_QK) && !bf16 && !f16)
+        return fail(GQA_ERR_UNSUPPORTED, "the matrix-core paths need bf16 or fp16 q/k/v");
+    if (path_req == GQA_PATH_MFMA_QK && f16)
+        return fail(GQA_ERR_UNSUPPORTED, "GQA_PATH_MFMA_QK reads bf16 only");
     if (fp8 && (path_req == GQA_PATH_VALU || path_req == GQA_PATH_MFMA_QK))
         return fail(GQA_ERR_UNSUPPORTED, "an fp8 cache runs on GQA_PATH_MFMA only");
 
     const int R = (int)R64;
-    // bf16 goes to the matrix cores (both products unless asked otherwise);
+    // bf16 and fp16 go to the matrix cores (both products unless asked otherwise);
     // fp32, or a forced VALU path, stays on the vector ALU
-    const bool mfma = bf16 && path_req != GQA_PATH_VALU;
+    const bool mfma = (bf16 || f16) && path_req != GQA_PATH_VALU;
     if (!mfma)
         p->path = gqa::Path::VALU;
     else if (path_req == GQA_PATH_MFMA_QK)
@@ -111,6 +116,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->path = gqa::Path::MFMA;
     p->kv_bf16 = bf16 && !fp8 ? 1 : 0;
     p->kv_fp8 = fp8 ? 1 : 0;
+    p->kv_f16 = f16 ? 1 : 0;
     p->src = src;
     p->D = s->D;
     p->R = R;
@@ -132,10 +138,12 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     // comparisons).
     {
         const char* mfx_env = getenv("GQA_MFX");
-        p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > 16 && !(mfx_env && mfx_env[0] == '0')) ? 1 : 0;
+        // (an fp16 cache has no 16 x 16 multi-wave kernel: it always takes the 32 x 32 one)
+        p->mfx = (p->path == gqa::Path::MFMA && !fp8 && src == 0 && R > 16 &&
+                  (f16 || !(mfx_env && mfx_env[0] == '0'))) ? 1 : 0;
     }
     if (p->mfx) p->row_block = R <= 32 ? 32 : R <= 64 ? 64 : R <= 128 ? 128 : 256;
-    // Up to 16 query rows of a plain bf16 cache of at most 128 MB: workgroups
+    // Up to 16 query rows of a plain bf16 / fp16 cache of at most 128 MB: workgroups
     // of 2 or 4 waves that split each piece's rows (one workgroup per 128 KB
     // of K/V, between half the compute units and all of them).  On such
     // caches a one-wave workgroup's stream is bound by its own load latency
@@ -346,7 +354,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan, srcx.src);
     if (st != GQA_OK) return st;
-    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
+    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8 || plan.kv_f16))
         return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 matrix-core path");
     if ((srcx.k_scale || srcx.v_scale) && !plan.kv_fp8)
         return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an fp8 cache only");

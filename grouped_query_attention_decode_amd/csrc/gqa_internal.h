@@ -53,6 +53,7 @@ struct Plan {
     Path path;
     int kv_bf16;        // 1: bf16 q/k/v, 0: fp32
     int kv_fp8;         // 1: bf16 q, fp8 E4M3 k/v codes with per-KV-head scales
+    int kv_f16;         // 1: fp16 q/k/v
     int D;
     int R;              // (H/G)*sq query rows per KV head
     int row_block;      // query rows per segment: a power of two <= 16 (vector ALU), 16, 32, 64 or 128 (MFMA)
@@ -116,7 +117,7 @@ int resident_groups_per_cu(const Plan& plan);
 inline int cache_rows_per_wave_tile(const Plan& p)
 {
     if (p.path != Path::VALU) return 16;
-    const int es = p.kv_bf16 ? 2 : 4;
+    const int es = (p.kv_bf16 || p.kv_f16) ? 2 : 4;
     const int lpt = p.D * es / 16;
     return kSlotsPerLane * (kWave / lpt);
 }

@@ -175,6 +175,32 @@ struct Bf16 {
     }
 };
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+struct F16 {
+    static constexpr int kBytes = 2;
+    static constexpr int kPerLoad = 8;
+    // <a, b> over 8 fp16 pairs, accumulated in fp32 (v_dot2_f32_f16).
+    static __device__ __forceinline__ float dot(const uint4& a, const uint4& b, float c)
+    {
+        c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.x), __builtin_bit_cast(f16x2_t, b.x), c, false);
+        c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.y), __builtin_bit_cast(f16x2_t, b.y), c, false);
+        c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.z), __builtin_bit_cast(f16x2_t, b.z), c, false);
+        c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.w), __builtin_bit_cast(f16x2_t, b.w), c, false);
+        return c;
+    }
+    static __device__ __forceinline__ void unpack(const uint4& a, float* f)
+    {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
+            f[2 * i] = (float)h[0];
+            f[2 * i + 1] = (float)h[1];
+        }
+    }
+};
+
 struct F32 {
     static constexpr int kBytes = 4;
     static constexpr int kPerLoad = 4;
@@ -1425,6 +1451,74 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+// The 16-bit operands of the matrix-core products: bf16 (a bf16 cache, and
+// the fp8 cache decoded to bf16) or fp16.  pack2 rounds two floats to nearest
+// even (element 0 in the low half), lo / hi give the value of element 0 / 1
+// of a packed pair; the products accumulate in fp32.
+//   mma16x32: v_mfma_f32_16x16x32_{bf16,f16}   (8 elements per lane)
+//   mma16x16: v_mfma_f32_16x16x16_{bf16,f16}   (4 elements per lane)
+//   mma32x16: v_mfma_f32_32x32x16_{bf16,f16}   (8 elements per lane)
+template <bool F16>
+struct Mx {
+    static __device__ __forceinline__ uint32_t pack2(float x0, float x1) { return pack_bf16x2(x0, x1); }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    // the rounding residuals x0 - lo(w), x1 - hi(w), packed
+    static __device__ __forceinline__ uint32_t resid2(float x0, float x1, uint32_t w)
+    {
+        return pack2(x0 - lo(w), x1 - hi(w));
+    }
+    static __device__ __forceinline__ f32x4_t mma16x32(const uint4& a, const uint4& b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mma16x16(const uint2& a, const uint2& b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                         c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x16_t mma32x16(const uint4& a, const uint4& b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mx<true> {
+    static __device__ __forceinline__ uint32_t pack2(float x0, float x1)
+    {
+        const f32x2_t v = {x0, x1};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+    static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
+    static __device__ __forceinline__ uint32_t resid2(float x0, float x1, uint32_t w)
+    {
+        return pack2(x0 - lo(w), x1 - hi(w));
+    }
+    static __device__ __forceinline__ f32x4_t mma16x32(const uint4& a, const uint4& b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                      0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mma16x16(const uint2& a, const uint2& b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                     0, 0);
+    }
+    static __device__ __forceinline__ f32x16_t mma32x16(const uint4& a, const uint4& b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                      0, 0, 0);
+    }
+};
+
 // Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950
 // row-swap permutes (VALU only).  The two results of a swap of x with itself
 // hold, in every lane, its own value and its partner's, so combining them
@@ -1458,11 +1552,13 @@ __device__ __forceinline__ float sum_x32(float x)
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
-template <int D, int NB, int SRC, bool KV8, int NW = 1, class SM = MfaShared<D>>
+template <int D, int NB, int SRC, bool KV8, int NW = 1, class SM = MfaShared<D>, bool F16 = false>
 __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb, const Piece& pc,
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
-    static_assert(NW == 1 || (SRC == kSrcCache && !KV8), "row-split workgroups read a plain bf16 cache");
+    static_assert(NW == 1 || (SRC == kSrcCache && !KV8), "row-split workgroups read a plain 16-bit cache");
+    static_assert(!F16 || (SRC == kSrcCache && !KV8), "an fp16 cache is read plain");
+    using MX = Mx<F16>;
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
     constexpr int SE = MfaShared<D>::SE;
@@ -1663,9 +1759,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
                 s4[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int s = 0; s < NK; ++s)
-                    s4[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[h][s]),
-                                                                    __builtin_bit_cast(bf16x8_t, qb[nb][s]), s4[h], 0, 0,
-                                                                    0);
+                    s4[h] = MX::mma16x32(kk[h][s], qb[nb][s], s4[h]);
             }
             float sc[4 * NH];
             float mx = -INFINITY;
@@ -1705,9 +1799,8 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
             }
 #pragma unroll
             for (int q = 0; q < 2 * NH; ++q) {
-                hw[nb][q] = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
-                lw[nb][q] = pack_bf16x2(pv[2 * q] - __uint_as_float(hw[nb][q] << 16),
-                                        pv[2 * q + 1] - __uint_as_float(hw[nb][q] & 0xFFFF0000u));
+                hw[nb][q] = MX::pack2(pv[2 * q], pv[2 * q + 1]);
+                lw[nb][q] = MX::resid2(pv[2 * q], pv[2 * q + 1], hw[nb][q]);
             }
         }
         // lane (kg, col) addresses row 4 kg + col / 4 (of each half), columns
@@ -1719,22 +1812,17 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
             const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * c));
             if constexpr (NH == 2) {
                 const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vr + 16 * SE + 16 * c));
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[nb][0], hw[nb][1], hw[nb][2], hw[nb][3]));
-                    const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[nb][0], lw[nb][1], lw[nb][2], lw[nb][3]));
-                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[nb][c], 0, 0, 0);
-                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[nb][c], 0, 0, 0);
+                    acc[nb][c] = MX::mma16x32(va, make_uint4(hw[nb][0], hw[nb][1], hw[nb][2], hw[nb][3]), acc[nb][c]);
+                    acc[nb][c] = MX::mma16x32(va, make_uint4(lw[nb][0], lw[nb][1], lw[nb][2], lw[nb][3]), acc[nb][c]);
                 }
             } else {
-                const s16x4_t va = __builtin_bit_cast(s16x4_t, v0);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(hw[nb][0], hw[nb][1]));
-                    const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(lw[nb][0], lw[nb][1]));
-                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[nb][c], 0, 0, 0);
-                    acc[nb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[nb][c], 0, 0, 0);
+                    acc[nb][c] = MX::mma16x16(v0, make_uint2(hw[nb][0], hw[nb][1]), acc[nb][c]);
+                    acc[nb][c] = MX::mma16x16(v0, make_uint2(lw[nb][0], lw[nb][1]), acc[nb][c]);
                 }
             }
         }
@@ -1964,7 +2052,7 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NB, int SRC, bool KV8>
+template <int D, int NB, int SRC, bool KV8, bool F16 = false>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const int32_t* __restrict__ lens_in, const int nB, const int nT, const Args a, const int R, const int n_rb)
 {
@@ -1990,7 +2078,7 @@ decode_mfa(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB, SRC, KV8>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB, SRC, KV8, 1, MfaShared<D>, F16>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
             partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -2003,7 +2091,7 @@ decode_mfa(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
 // caches, where a one-wave workgroup's stream is bound by its own load
 // latency and per-tile chain rather than by HBM, this puts NW waves' loads in
 // flight per workgroup without adding pieces, partials or merges.
-template <int D, int NB, int NW>
+template <int D, int NB, int NW, bool F16 = false>
 __global__ void __launch_bounds__(kWave * NW)
 decode_mfs(const int32_t* __restrict__ lens_in, const int nB, const int nT, const Args a, const int R, const int n_rb)
 {
@@ -2024,7 +2112,8 @@ decode_mfs(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB, kSrcCache, false, NW>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB, kSrcCache, false, NW, MfsShared<D, NB, NW>, F16>(a, sm, R, n_rb, pc, cm, chunk, &pd) &&
+            !a.deferred) {
             partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -2351,8 +2440,6 @@ decode_mfw(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
 // lanes start 16 banks apart); the row-contiguous stores of 16 lanes cover
 // one row.
 // ---------------------------------------------------------------------------
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 template <int D>
 struct MfxGeom {
     static constexpr int TR = 32;               // cache rows per tile
@@ -2385,11 +2472,6 @@ struct MfxShared {
     int merge;                            // 1 when this workgroup arrived last for the current piece
 };
 
-__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-}
 
 // Tiles of loads in flight per thread: one per wave when each wave streams
 // its own tiles (64 registers each); two when waves share a tile (four, with
@@ -2398,7 +2480,7 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
 template <int NQ>
 constexpr int mfx_reg_tiles() { return NQ == 1 ? 1 : 2; }
 
-template <int D, int QB, int NQ, int NS>
+template <int D, int QB, int NQ, int NS, bool F16 = false>
 __device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS>& sm, int R, const Piece& pc,
                                           const ChunkMap& cm, int chunk, int n_rb, Pending* pd)
 {
@@ -2505,7 +2587,7 @@ __device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS
         for (int s = 0; s < NKS; ++s) {
             const uint4 kop = *reinterpret_cast<const uint4*>(kt + col * SK + (2 * s + hf) * 16);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s16q[qb] = mfma32(kop, qop[qb][s], s16q[qb]);
+            for (int qb = 0; qb < QB; ++qb) s16q[qb] = Mx<F16>::mma32x16(kop, qop[qb][s], s16q[qb]);
         }
         uint32_t ph[QB][8], pl[QB][8];
 #pragma unroll
@@ -2557,9 +2639,8 @@ __device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS
             l_run[qb] += ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                ph[qb][q] = pack_bf16x2(p[2 * q], p[2 * q + 1]);
-                pl[qb][q] = pack_bf16x2(p[2 * q] - __uint_as_float(ph[qb][q] << 16),
-                                        p[2 * q + 1] - __uint_as_float(ph[qb][q] & 0xFFFF0000u));
+                ph[qb][q] = Mx<F16>::pack2(p[2 * q], p[2 * q + 1]);
+                pl[qb][q] = Mx<F16>::resid2(p[2 * q], p[2 * q + 1], ph[qb][q]);
             }
         }
         // V^T: in each 16-lane group (h, cb) lane j addresses tile row
@@ -2581,9 +2662,9 @@ __device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS
                 const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    acc[qb][db] = mfma32(va, make_uint4(ph[qb][4 * u], ph[qb][4 * u + 1], ph[qb][4 * u + 2],
+                    acc[qb][db] = Mx<F16>::mma32x16(va, make_uint4(ph[qb][4 * u], ph[qb][4 * u + 1], ph[qb][4 * u + 2],
                                                         ph[qb][4 * u + 3]), acc[qb][db]);
-                    acc[qb][db] = mfma32(va, make_uint4(pl[qb][4 * u], pl[qb][4 * u + 1], pl[qb][4 * u + 2],
+                    acc[qb][db] = Mx<F16>::mma32x16(va, make_uint4(pl[qb][4 * u], pl[qb][4 * u + 1], pl[qb][4 * u + 2],
                                                         pl[qb][4 * u + 3]), acc[qb][db]);
                 }
             }
@@ -2788,7 +2869,7 @@ __device__ __forceinline__ bool mfx_piece(const Args& a, MfxShared<D, QB, NQ, NS
     return true;
 }
 
-template <int D, int QB, int NQ, int NS>
+template <int D, int QB, int NQ, int NS, bool F16 = false>
 __global__ void __launch_bounds__(kWave * NQ * NS) __attribute__((amdgpu_waves_per_eu(NQ * NS / 4, NQ * NS / 4)))
 decode_mfx(const int32_t* __restrict__ lens_in, const int nB, const int nT, const Args a, const int R, const int n_rb)
 {
@@ -2812,7 +2893,7 @@ decode_mfx(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
-        if (mfx_piece<D, QB, NQ, NS>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
+        if (mfx_piece<D, QB, NQ, NS, F16>(a, sm, R, pc, cm, chunk, n_rb, &pd) && !a.deferred) {
             partials_stored_before_arrival();    // this wave's partial stores complete at device scope
             __syncthreads();                     // ... and every other wave's
             if (tid == 0) {
@@ -2987,40 +3068,51 @@ static DecodeFn pick_mqk(int rb)
     }
 }
 
-template <int SRC, bool KV8>
+template <int SRC, bool KV8, bool F16 = false>
 static DecodeFn pick_mfa(const Plan& p)
 {
     switch (p.row_block) {
-    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC, KV8> : decode_mfa<128, 1, SRC, KV8>;
-    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC, KV8> : decode_mfa<128, 2, SRC, KV8>;
-    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC, KV8> : decode_mfa<128, 4, SRC, KV8>;
+    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC, KV8, F16> : decode_mfa<128, 1, SRC, KV8, F16>;
+    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC, KV8, F16> : decode_mfa<128, 2, SRC, KV8, F16>;
+    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC, KV8, F16> : decode_mfa<128, 4, SRC, KV8, F16>;
     default: return nullptr;
     }
 }
 
-template <int D>
+template <int D, bool F16>
 static DecodeFn pick_mfx(int row_block)
 {
     switch (row_block) {
-    case 32: return decode_mfx<D, 1, 1, 4>;
-    case 64: return decode_mfx<D, 1, 2, 2>;
-    case 128: return decode_mfx<D, 1, 4, 2>;
-    case 256: return decode_mfx<D, 1, 8, 1>;
+    case 32: return decode_mfx<D, 1, 1, 4, F16>;
+    case 64: return decode_mfx<D, 1, 2, 2, F16>;
+    case 128: return decode_mfx<D, 1, 4, 2, F16>;
+    case 256: return decode_mfx<D, 1, 8, 1, F16>;
     default: return nullptr;
     }
+}
+
+template <bool F16>
+static DecodeFn pick_mfs(const Plan& p)
+{
+    if (p.rsplit == 2) return p.D == 64 ? decode_mfs<64, 1, 2, F16> : decode_mfs<128, 1, 2, F16>;
+    if (p.rsplit == 4) return p.D == 64 ? decode_mfs<64, 1, 4, F16> : decode_mfs<128, 1, 4, F16>;
+    return nullptr;
 }
 
 static DecodeFn pick(const Plan& p)
 {
+    // an fp16 cache: plain layout only, on the 32 x 32, row-split and
+    // one-block matrix-core kernels or the vector-ALU kernel
+    if (p.kv_f16 && (p.src != kSrcCache || p.path == Path::MFMA_QK)) return nullptr;
     if (p.path == Path::MFMA && p.mfx) {
-        if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
-        return p.D == 64 ? pick_mfx<64>(p.row_block) : pick_mfx<128>(p.row_block);
+        if (!(p.kv_bf16 || p.kv_f16) || p.src != kSrcCache) return nullptr;
+        if (p.kv_f16) return p.D == 64 ? pick_mfx<64, true>(p.row_block) : pick_mfx<128, true>(p.row_block);
+        return p.D == 64 ? pick_mfx<64, false>(p.row_block) : pick_mfx<128, false>(p.row_block);
     }
     if (p.path == Path::MFMA && p.rsplit > 1) {
-        if (!p.kv_bf16 || p.src != kSrcCache || p.row_block != 16 || p.wg_waves != p.rsplit) return nullptr;
-        if (p.rsplit == 2) return p.D == 64 ? decode_mfs<64, 1, 2> : decode_mfs<128, 1, 2>;
-        if (p.rsplit == 4) return p.D == 64 ? decode_mfs<64, 1, 4> : decode_mfs<128, 1, 4>;
-        return nullptr;
+        if (!(p.kv_bf16 || p.kv_f16) || p.src != kSrcCache || p.row_block != 16 || p.wg_waves != p.rsplit)
+            return nullptr;
+        return p.kv_f16 ? pick_mfs<true>(p) : pick_mfs<false>(p);
     }
     if (p.path == Path::MFMA && p.wg_waves > 1) {
         if (!p.kv_bf16 || p.src != kSrcCache) return nullptr;
@@ -3030,6 +3122,7 @@ static DecodeFn pick(const Plan& p)
     }
     if (p.path == Path::MFMA) {
         if (p.kv_fp8) return p.src == kSrcCache ? pick_mfa<kSrcCache, true>(p) : nullptr;
+        if (p.kv_f16) return pick_mfa<kSrcCache, false, true>(p);
         if (!p.kv_bf16) return nullptr;
         switch (p.src) {
         case kSrcCache: return pick_mfa<kSrcCache, false>(p);
@@ -3044,6 +3137,8 @@ static DecodeFn pick(const Plan& p)
     }
     if (p.kv_bf16)
         return p.D == 64 ? pick_valu<Bf16, 64>(p.row_block) : pick_valu<Bf16, 128>(p.row_block);
+    if (p.kv_f16)
+        return p.D == 64 ? pick_valu<F16, 64>(p.row_block) : pick_valu<F16, 128>(p.row_block);
     return p.D == 64 ? pick_valu<F32, 64>(p.row_block) : pick_valu<F32, 128>(p.row_block);
 }
 

@@ -40,8 +40,10 @@
  *   - seq_lens values outside [0, T] are clamped on the device.
  *
  * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
- * (F32, F32, F32), (BF16, BF16, F32) or (BF16, FP8_E4M3, F32) (the fp8
- * cache through gqa_decode_fp8, or gqa_decode with unit scales); H % G == 0;
+ * (F32, F32, F32), (BF16, BF16, F32), (F16, F16, F32) or
+ * (BF16, FP8_E4M3, F32) (the fp8 cache through gqa_decode_fp8, or
+ * gqa_decode with unit scales; appended tokens and paged caches bf16 only);
+ * H % G == 0;
  * any B >= 0, sq >= 1, T >= 1 with T * D < 2^31, B * H * sq * D < 2^40,
  * (H/G) * sq <= 2^20 and B * G * (row blocks per KV head) <= 2^18, where a
  * row block is 16 query rows on the vector-ALU path and 16, 32, 64 or 128
@@ -67,8 +69,13 @@ typedef enum {
 
 /* GQA_FP8_E4M3: OCP FP8 E4M3 ("E4M3FN") codes -- sign, 4 exponent bits with
  * bias 7, 3 mantissa bits, subnormals, no infinities; codes S.1111.111 are
- * NaN and must not appear in the rows read.  A cache only. */
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2 } gqa_dtype_t;
+ * NaN and must not appear in the rows read.  A cache only.
+ * GQA_F16: IEEE binary16, for q, k and v together (the 4 MB K cache of
+ * [1, 8, 4096, 64] in the repeat_kv example of "Same GQA, Different
+ * Execution Cost Across Backends", section 2, holds 2-byte values of a type
+ * the page does not name); both products on the matrix cores in fp16 with
+ * fp32 accumulation, the softmax weights as an fp16 pair hi + lo. */
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2, GQA_F16 = 3 } gqa_dtype_t;
 
 /* Problem shape.  H: query heads, G: KV heads ("num_key_value_heads"),
  * sq: new query tokens per sequence, T: cache capacity in rows, D: head dim. */

@@ -327,6 +327,46 @@ def test_injected_workspace_allocation_failure(lib, monkeypatch):
         assert st == gqa.GQA_ERR_HIP
 
 
+def test_plan_fp16(lib):
+    """fp16 q/k/v plan exactly as bf16 does (the same grids, kernels and
+    workspaces: the matrix-core kernels take either 2-byte type); above 16
+    query rows per KV head the 32 x 32 kernel runs even when GQA_MFX=0 asks
+    bf16 for the 16 x 16 one.  fp16 has no scores-only matrix path, no
+    appended-token or paged form, and mixes with no other type."""
+    f16 = dict(q_dtype=gqa.GQA_F16, kv_dtype=gqa.GQA_F16)
+    for kw in (dict(B=32), dict(B=1, D=64), dict(B=4, D=128), dict(B=64, G=1, T=8192),
+               dict(B=16, G=1, sq=2, T=16384), dict(B=8, sq=64), dict(B=1, T=100)):
+        assert gqa.plan(_shape(**kw, **f16)) == gqa.plan(_shape(**kw)), kw
+        assert gqa.workspace_bytes(_shape(**kw, **f16)) == gqa.workspace_bytes(_shape(**kw))
+    v = gqa.plan(_shape(**f16), path=gqa.PATH_VALU)
+    assert v == gqa.plan(_shape(), path=gqa.PATH_VALU) and v["path"] == gqa.PATH_VALU
+    import os
+    mqa = dict(B=64, G=1, T=8192)
+    mfx = gqa.plan(_shape(**mqa))
+    assert mfx["waves_per_group"] == 4
+    os.environ["GQA_MFX"] = "0"
+    try:
+        assert gqa.plan(_shape(**mqa))["waves_per_group"] == 1
+        assert gqa.plan(_shape(**mqa, **f16)) == mfx
+    finally:
+        del os.environ["GQA_MFX"]
+    with pytest.raises(gqa.GqaError) as ei:
+        gqa.plan(_shape(**f16), path=gqa.PATH_MFMA_QK)
+    assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+    for q_dt, kv_dt, out_dt in ((gqa.GQA_F16, gqa.GQA_BF16, gqa.GQA_F32), (gqa.GQA_BF16, gqa.GQA_F16, gqa.GQA_F32),
+                                (gqa.GQA_F16, gqa.GQA_FP8_E4M3, gqa.GQA_F32), (gqa.GQA_F16, gqa.GQA_F16, gqa.GQA_F16),
+                                (gqa.GQA_F32, gqa.GQA_F16, gqa.GQA_F32)):
+        s = _shape(q_dtype=q_dt, kv_dtype=kv_dt, out_dtype=out_dt)
+        with pytest.raises(gqa.GqaError) as ei:
+            gqa.plan(s)
+        assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+        assert "F16,F16,F32" in lib.gqa_last_error().decode()
+    assert gqa.append_workspace_bytes(_shape(B=32, **f16)) == 0
+    assert "bf16" in lib.gqa_last_error().decode()
+    ps = gqa.PagedShape(32, 32, 8, 1, 128, 16, 8192, 256, gqa.GQA_F16, gqa.GQA_F16, gqa.GQA_F32)
+    assert gqa.paged_workspace_bytes(ps) == 0
+
+
 def test_append_workspace_bytes(lib):
     """Appended tokens above 16 query rows per KV head run one-wave
     workgroups of up to 64 rows, not the plain decode's 32 x 32 kernel:
