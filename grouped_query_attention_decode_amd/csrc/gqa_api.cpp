@@ -76,8 +76,6 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         return fail(GQA_ERR_UNSUPPORTED,
                     "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32), (BF16,BF16,F32), "
                     "(F16,F16,F32) or (BF16,FP8_E4M3,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
-    if (f16 && src != 0)
-        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need a bf16 cache");
     if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
         return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
     if ((int64_t)s->B * s->H * s->sq * s->D >= (int64_t)1 << 40)
@@ -354,8 +352,8 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan, srcx.src);
     if (st != GQA_OK) return st;
-    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8 || plan.kv_f16))
-        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 matrix-core path");
+    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
+        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 / fp16 matrix-core path");
     if ((srcx.k_scale || srcx.v_scale) && !plan.kv_fp8)
         return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an fp8 cache only");
     plan.src = srcx.src;

@@ -1557,7 +1557,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
     static_assert(NW == 1 || (SRC == kSrcCache && !KV8), "row-split workgroups read a plain 16-bit cache");
-    static_assert(!F16 || (SRC == kSrcCache && !KV8), "an fp16 cache is read plain");
+    static_assert(!F16 || !KV8, "an fp8 cache takes bf16 queries");
     using MX = Mx<F16>;
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
@@ -3101,9 +3101,10 @@ static DecodeFn pick_mfs(const Plan& p)
 
 static DecodeFn pick(const Plan& p)
 {
-    // an fp16 cache: plain layout only, on the 32 x 32, row-split and
-    // one-block matrix-core kernels or the vector-ALU kernel
-    if (p.kv_f16 && (p.src != kSrcCache || p.path == Path::MFMA_QK)) return nullptr;
+    // an fp16 cache: on the 32 x 32, row-split and one-block matrix-core
+    // kernels (appended tokens and paged caches on the one-block kernel) or
+    // the vector-ALU kernel
+    if (p.kv_f16 && p.path == Path::MFMA_QK) return nullptr;
     if (p.path == Path::MFMA && p.mfx) {
         if (!(p.kv_bf16 || p.kv_f16) || p.src != kSrcCache) return nullptr;
         if (p.kv_f16) return p.D == 64 ? pick_mfx<64, true>(p.row_block) : pick_mfx<128, true>(p.row_block);
@@ -3122,7 +3123,14 @@ static DecodeFn pick(const Plan& p)
     }
     if (p.path == Path::MFMA) {
         if (p.kv_fp8) return p.src == kSrcCache ? pick_mfa<kSrcCache, true>(p) : nullptr;
-        if (p.kv_f16) return pick_mfa<kSrcCache, false, true>(p);
+        if (p.kv_f16) {
+            switch (p.src) {
+            case kSrcCache: return pick_mfa<kSrcCache, false, true>(p);
+            case kSrcAppend: return pick_mfa<kSrcAppend, false, true>(p);
+            case kSrcPaged: return pick_mfa<kSrcPaged, false, true>(p);
+            default: return nullptr;
+            }
+        }
         if (!p.kv_bf16) return nullptr;
         switch (p.src) {
         case kSrcCache: return pick_mfa<kSrcCache, false>(p);

@@ -42,7 +42,8 @@
  * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
  * (F32, F32, F32), (BF16, BF16, F32), (F16, F16, F32) or
  * (BF16, FP8_E4M3, F32) (the fp8 cache through gqa_decode_fp8, or
- * gqa_decode with unit scales; appended tokens and paged caches bf16 only);
+ * gqa_decode with unit scales; appended tokens and paged caches bf16 or
+ * fp16);
  * H % G == 0;
  * any B >= 0, sq >= 1, T >= 1 with T * D < 2^31, B * H * sq * D < 2^40,
  * (H/G) * sq <= 2^20 and B * G * (row blocks per KV head) <= 2^18, where a
@@ -230,7 +231,8 @@ gqa_status_t gqa_decode_noalloc(const gqa_shape_t *shape, const void *q,
  * loop's append-then-attend step ("GQA (Grouped-Query Attention) 분석",
  * section "동작 원리", items 2 "Projection과 RoPE" and 3 "Incremental
  * decode").
- * bf16 only (GQA_PATH_MFMA; another path is GQA_ERR_UNSUPPORTED).
+ * bf16 or fp16 (GQA_PATH_MFMA; another path or dtype is
+ * GQA_ERR_UNSUPPORTED).
  * workspace NULL with ws_bytes 0: the library-owned workspace.
  */
 gqa_status_t gqa_decode_append(const gqa_shape_t *shape, const void *q,
@@ -281,7 +283,7 @@ size_t gqa_paged_workspace_bytes(const gqa_paged_shape_t *shape);
  * "GQA (Grouped-Query Attention) 분석", section "장단점" and the checklist
  * of item 4 of "동작 원리").  Only the table entries for rows below L_b are
  * read; an entry outside [0, num_pages) is clamped into it (no fault, but
- * the result is then meaningless).  bf16 only (GQA_PATH_MFMA).
+ * the result is then meaningless).  bf16 or fp16 (GQA_PATH_MFMA).
  * workspace NULL with ws_bytes 0: the library-owned workspace.
  */
 gqa_status_t gqa_decode_paged(const gqa_paged_shape_t *shape, const void *q,

@@ -331,8 +331,9 @@ def test_plan_fp16(lib):
     """fp16 q/k/v plan exactly as bf16 does (the same grids, kernels and
     workspaces: the matrix-core kernels take either 2-byte type); above 16
     query rows per KV head the 32 x 32 kernel runs even when GQA_MFX=0 asks
-    bf16 for the 16 x 16 one.  fp16 has no scores-only matrix path, no
-    appended-token or paged form, and mixes with no other type."""
+    bf16 for the 16 x 16 one; appended tokens and paged caches plan as
+    bf16 too.  fp16 has no scores-only matrix path and mixes with no other
+    type."""
     f16 = dict(q_dtype=gqa.GQA_F16, kv_dtype=gqa.GQA_F16)
     for kw in (dict(B=32), dict(B=1, D=64), dict(B=4, D=128), dict(B=64, G=1, T=8192),
                dict(B=16, G=1, sq=2, T=16384), dict(B=8, sq=64), dict(B=1, T=100)):
@@ -361,10 +362,12 @@ def test_plan_fp16(lib):
             gqa.plan(s)
         assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
         assert "F16,F16,F32" in lib.gqa_last_error().decode()
-    assert gqa.append_workspace_bytes(_shape(B=32, **f16)) == 0
-    assert "bf16" in lib.gqa_last_error().decode()
-    ps = gqa.PagedShape(32, 32, 8, 1, 128, 16, 8192, 256, gqa.GQA_F16, gqa.GQA_F16, gqa.GQA_F32)
-    assert gqa.paged_workspace_bytes(ps) == 0
+    for kw in (dict(B=32), dict(B=16, G=1, sq=2), dict(B=8, sq=64)):
+        a = gqa.append_workspace_bytes(_shape(**kw, **f16))
+        assert a > 0 and a == gqa.append_workspace_bytes(_shape(**kw))
+    ps = dict(B=32, H=32, G=8, sq=1, D=128, page_size=16, num_pages=8192, max_pages=256, out_dtype=gqa.GQA_F32)
+    a = gqa.paged_workspace_bytes(gqa.PagedShape(q_dtype=gqa.GQA_F16, kv_dtype=gqa.GQA_F16, **ps))
+    assert a > 0 and a == gqa.paged_workspace_bytes(gqa.PagedShape(q_dtype=gqa.GQA_BF16, kv_dtype=gqa.GQA_BF16, **ps))
 
 
 def test_append_workspace_bytes(lib):

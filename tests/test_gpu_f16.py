@@ -3,7 +3,8 @@
 The matrix-core kernels take fp16 operands where they take bf16 ones
 (v_mfma_f32_{16x16x32,16x16x16,32x32x16}_f16, fp32 accumulation) and the
 vector-ALU kernel accumulates fp16 pairs in fp32 (v_dot2_f32_f16); the
-softmax weights enter the V product as an fp16 pair hi + lo.
+softmax weights enter the V product as an fp16 pair hi + lo.  The appended-
+token and paged entry points take fp16 on the one-block kernel.
 
 Tolerance 2e-4 (max abs error), derived from the arithmetic: the q.k and
 p.v products of fp16 values are exact in fp32 and the weights carry ~22
@@ -196,13 +197,82 @@ def test_f16_poisoned_tail_is_never_read(gqa, path_name):
 
 
 def test_f16_unsupported_forms_refused(gqa):
-    """fp16 has no appended-token, paged or scores-only matrix form: each is
-    refused with GQA_ERR_UNSUPPORTED before any device work."""
+    """fp16 has no scores-only matrix form and does not mix with an fp8
+    cache: each is refused with GQA_ERR_UNSUPPORTED before any device work."""
     x = _to(gi.make_custom(2, 32, 8, 128, 64, 1, dtype="f16", seed=3, seq_lens=[10, 20]), "cuda")
     with pytest.raises(gqa.GqaError) as ei:
         gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], path=gqa.PATH_MFMA_QK)
     assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
-    kn = torch.zeros(2, 8, 1, 128, dtype=torch.float16, device="cuda")
+    codes = torch.zeros(2, 8, 64, 128, dtype=torch.uint8, device="cuda")
     with pytest.raises(gqa.GqaError) as ei:
-        gqa.decode_append(x["q"], kn, kn, x["k"], x["v"], x["seq_lens"])
+        gqa.decode_fp8(x["q"], codes, codes.clone(), seq_lens=x["seq_lens"])
     assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+
+
+APPEND = [
+    # B, H, G, D, T, sq, seq_lens
+    (3, 32, 8, 128, 600, 1, [600, 257, 1]),
+    (2, 32, 8, 64, 300, 2, [300, 2]),
+    (2, 32, 1, 128, 150, 2, [150, 77]),          # 64 rows, combine kernel
+    (2, 8, 2, 128, 400, 64, [400, 70]),          # 64 new tokens, 256 rows
+    (2, 4, 1, 64, 90, 8, [90, 5]),               # L < sq: three tokens dropped
+]
+
+
+@pytest.mark.parametrize("case", APPEND, ids=lambda c: "B%d_H%d_G%d_D%d_T%d_sq%d" % c[:6])
+def test_f16_append(gqa, orc, case):
+    """gqa_decode_append with fp16 q/k/v: the output against the oracle's
+    append-then-attend, and the cache rows it writes bit for bit."""
+    B, H, G, D, T, sq, lens = case
+    x = gi.make_custom(B, H, G, D, T, sq, dtype="f16", seed=640 + T + sq, seq_lens=lens)
+    gen = torch.Generator().manual_seed(641 + sq)
+    kn = torch.randn(B, G, sq, D, generator=gen).to(torch.float16)
+    vn = torch.randn(B, G, sq, D, generator=gen).to(torch.float16)
+    want, k_after, v_after = orc.decode_append_f64(x["q"], kn, vn, x["k"], x["v"], x["seq_lens"],
+                                                   1.0 / math.sqrt(D), threads=8)
+    kc, vc = x["k"].cuda(), x["v"].cuda()
+    got = gqa.decode_append(x["q"].cuda(), kn.cuda(), vn.cuda(), kc, vc, x["seq_lens"].cuda())
+    torch.cuda.synchronize()
+    _compare(got, want, "append %s" % (case,))
+    assert np.array_equal(kc.double().cpu().numpy(), k_after)
+    assert np.array_equal(vc.double().cpu().numpy(), v_after)
+    assert kc.dtype == torch.float16
+
+
+def _to_pages(k, ps, perm):
+    B, G, T, D = k.shape
+    n = T // ps
+    pages = torch.empty(B * n, G, ps, D, dtype=k.dtype)
+    bt = torch.empty(B, n, dtype=torch.int32)
+    for b in range(B):
+        for i in range(n):
+            p = int(perm[b * n + i])
+            pages[p] = k[b, :, i * ps:(i + 1) * ps]
+            bt[b, i] = p
+    return pages, bt
+
+
+PAGED = [
+    # B, H, G, D, T, sq, page_size, seq_lens
+    (3, 32, 8, 128, 512, 1, 16, [512, 300, 17]),
+    (2, 32, 8, 64, 512, 2, 64, [512, 65]),
+    (2, 32, 1, 128, 320, 2, 32, [320, 33]),
+    (2, 8, 2, 128, 256, 64, 16, [256, 100]),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: "B%d_H%d_G%d_D%d_T%d_sq%d_ps%d" % c[:7])
+def test_f16_paged(gqa, orc, case):
+    """gqa_decode_paged with fp16 q/k/v, pages in random order and table
+    entries past each sequence's length poisoned, against the oracle."""
+    B, H, G, D, T, sq, ps, lens = case
+    x = gi.make_custom(B, H, G, D, T, sq, dtype="f16", seed=650 + T + ps, seq_lens=lens)
+    perm = np.random.default_rng(ps + 1).permutation(B * (T // ps))
+    kp, bt = _to_pages(x["k"], ps, perm)
+    vp, _ = _to_pages(x["v"], ps, perm)
+    for b, L in enumerate(lens):
+        bt[b, (L + ps - 1) // ps:] = -7
+    want = orc.decode_paged_f64(x["q"], kp, vp, bt, x["seq_lens"], threads=8)
+    got = gqa.decode_paged(x["q"].cuda(), kp.cuda(), vp.cuda(), bt.cuda(), x["seq_lens"].cuda())
+    torch.cuda.synchronize()
+    _compare(got, want, "paged %s" % (case,))
