@@ -3,8 +3,9 @@ float64 oracle: gqa_decode, gqa_decode_append, gqa_decode_paged and
 gqa_decode_fp8, with random group sizes, head dims, context lengths (ragged,
 with empty and single-row sequences), new-token counts, page sizes, grid
 sizes and merge modes -- so that tile ends, row windows, page windows and
-split points fall at arbitrary rows.  Tolerance as for the fixed cases
-(bf16 inputs, fp32 accumulation: 2e-3 max abs; fp32: 1e-5)."""
+split points fall at arbitrary rows; the fp16 entry points on the same
+shapes.  Tolerance as for the fixed cases (bf16 inputs, fp32 accumulation:
+2e-3 max abs; fp16: 2e-4; fp32: 1e-5)."""
 import math
 
 import numpy as np
@@ -14,7 +15,7 @@ import torch
 import gqa_inputs as gi
 
 pytestmark = pytest.mark.gpu
-TOL = {"bf16": 2e-3, "f32": 1e-5}
+TOL = {"bf16": 2e-3, "f16": 2e-4, "f32": 1e-5}
 N_CASES = 24
 
 
@@ -94,31 +95,50 @@ def test_random_decode_other_kernels(gqa, orc, monkeypatch, i, forced):
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_random_append(gqa, orc, i):
+def test_random_f16(gqa, orc, i):
+    """fp16 q/k/v on the same shapes: the default plan, or (every third
+    case) the vector-ALU kernel forced."""
+    c = _shape(i)
+    x = gi.make_custom(c["B"], c["H"], c["G"], c["D"], c["T"], c["sq"], dtype="f16", seed=c["seed"],
+                       seq_lens=c["lens"])
+    want = orc.decode_f64(x["q"], x["k"], x["v"], x["seq_lens"], 1.0 / math.sqrt(c["D"]))
+    path = gqa.PATH_VALU if i % 3 == 0 else gqa.PATH_AUTO
+    kw = dict(workgroups=c["P"], path=path)
+    if path == gqa.PATH_AUTO:
+        kw["merge"] = c["merge"]
+    got = gqa.decode(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["seq_lens"].cuda(), **kw)
+    torch.cuda.synchronize()
+    assert _err(got, want) <= TOL["f16"], (c, path)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_append(gqa, orc, i, dt):
     c = _shape(i)
     B, G, D, T, sq = c["B"], c["G"], c["D"], c["T"], c["sq"]
-    x = gi.make_custom(B, c["H"], G, D, T, sq, dtype="bf16", seed=c["seed"], seq_lens=c["lens"])
+    x = gi.make_custom(B, c["H"], G, D, T, sq, dtype=dt, seed=c["seed"], seq_lens=c["lens"])
     gen = torch.Generator().manual_seed(c["seed"] + 1)
-    kn = torch.randn(B, G, sq, D, generator=gen).to(torch.bfloat16)
-    vn = torch.randn(B, G, sq, D, generator=gen).to(torch.bfloat16)
+    kn = torch.randn(B, G, sq, D, generator=gen).to(x["k"].dtype)
+    vn = torch.randn(B, G, sq, D, generator=gen).to(x["k"].dtype)
     want, k_after, v_after = orc.decode_append_f64(x["q"], kn, vn, x["k"], x["v"], x["seq_lens"],
                                                    1.0 / math.sqrt(D), threads=8)
     kc, vc = x["k"].cuda(), x["v"].cuda()
     got = gqa.decode_append(x["q"].cuda(), kn.cuda(), vn.cuda(), kc, vc, x["seq_lens"].cuda(),
                             workgroups=c["P"], merge=c["merge"])
     torch.cuda.synchronize()
-    assert _err(got, want) <= TOL["bf16"], c
+    assert _err(got, want) <= TOL[dt], c
     assert np.array_equal(kc.double().cpu().numpy(), k_after), c
     assert np.array_equal(vc.double().cpu().numpy(), v_after), c
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_random_paged(gqa, orc, i):
+def test_random_paged(gqa, orc, i, dt):
     c = _shape(i)
     B, G, D, T = c["B"], c["G"], c["D"], c["T"]
     ps = int(np.random.default_rng(c["seed"]).choice([16, 32, 64, 256]))
     n = (T + ps - 1) // ps
-    x = gi.make_custom(B, c["H"], G, D, n * ps, c["sq"], dtype="bf16", seed=c["seed"],
+    x = gi.make_custom(B, c["H"], G, D, n * ps, c["sq"], dtype=dt, seed=c["seed"],
                        seq_lens=[min(L, n * ps) for L in c["lens"]])
     perm = np.random.default_rng(c["seed"] + 2).permutation(B * n)
     kp = torch.empty(B * n, G, ps, D, dtype=x["k"].dtype)
@@ -134,7 +154,7 @@ def test_random_paged(gqa, orc, i):
     got = gqa.decode_paged(x["q"].cuda(), kp.cuda(), vp.cuda(), bt.cuda(), x["seq_lens"].cuda(),
                            workgroups=c["P"], merge=c["merge"])
     torch.cuda.synchronize()
-    assert _err(got, want) <= TOL["bf16"], (c, ps)
+    assert _err(got, want) <= TOL[dt], (c, ps)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
