@@ -349,3 +349,15 @@ def test_bf16_inputs_are_upcast_exactly(oracle_mod):
     a = oracle_mod.decode_f64(q, k, v, sl)
     b = oracle_mod.decode_f64(q.float(), k.float(), v.float(), sl)
     assert np.array_equal(a, b)
+
+
+def test_f16_inputs_are_upcast_exactly(oracle_mod):
+    """fp16 inputs reach the oracle as the exact stored values (fp32 holds
+    every fp16 value, subnormals included)."""
+    q, k, v, sl = _draw(1, 8, 2, 16, 12, 1, seed=42, dtype="f16")
+    assert q.dtype == torch.float16
+    k[0, 0, 0, :4] = torch.tensor([6e-8, -3e-5, 65504.0, -1.0 / 3.0], dtype=torch.float16)
+    a = oracle_mod.decode_f64(q, k, v, sl)
+    b = oracle_mod.decode_f64(q.float(), k.float(), v.float(), sl)
+    assert np.array_equal(a, b)
+    assert oracle_mod._f64(k)[0, 0, 0, 0] == float(torch.tensor(6e-8, dtype=torch.float16).double())
