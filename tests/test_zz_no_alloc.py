@@ -44,6 +44,8 @@ CASES = [
     # the combine kernel), then a smaller ragged GQA-8 call (in-kernel merges)
     dict(B=16, H=32, G=1, D=128, T=2048, sq=1, seq_lens=[2048] * 16, seed=901),
     dict(B=3, H=32, G=8, D=128, T=1000, sq=1, seq_lens=[1000, 517, 1], seed=902),
+    # and an fp16 cache, smaller again
+    dict(B=2, H=32, G=8, D=64, T=500, sq=1, seq_lens=[500, 77], seed=904, dtype="f16"),
 ]
 
 
@@ -58,8 +60,8 @@ def test_noalloc_matches_decode_ex_twice(gqa):
     assert _call_noalloc(gqa, w, wout) == gqa.GQA_OK
     torch.cuda.synchronize()
     for i, c in enumerate(CASES):
-        x = gi.make_custom(c["B"], c["H"], c["G"], c["D"], c["T"], c["sq"], dtype="bf16", seed=c["seed"],
-                           seq_lens=c["seq_lens"], device="cuda")
+        x = gi.make_custom(c["B"], c["H"], c["G"], c["D"], c["T"], c["sq"], dtype=c.get("dtype", "bf16"),
+                           seed=c["seed"], seq_lens=c["seq_lens"], device="cuda")
         want = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"])
         out = torch.full(x["q"].shape, float("nan"), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
