@@ -253,10 +253,11 @@ def parity_spot_check(args, w, x, out, extra):
     b = 0
     xb = {k: v[b:b + 1].cpu() for k, v in x.items()}
     scale = 1.0 / math.sqrt(w.D)
-    if args.mode == "fp8":
+    if args.mode in ("fp8", "int8"):
         kq, vq, ks, vs = extra
-        want = oracle.decode_fp8_f64(xb["q"], kq[b:b + 1].cpu(), vq[b:b + 1].cpu(), ks.cpu(), vs.cpu(),
-                                     xb["seq_lens"], scale, threads=8)
+        fn = oracle.decode_fp8_f64 if args.mode == "fp8" else oracle.decode_int8_f64
+        want = fn(xb["q"], kq[b:b + 1].cpu(), vq[b:b + 1].cpu(), ks.cpu(), vs.cpu(), xb["seq_lens"], scale,
+                  threads=8)
     elif args.mode == "append":
         kn, vn = extra
         # the cache already holds the appended rows (every step stores the same ones)
@@ -279,7 +280,7 @@ def main(argv=None):
     ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_qk"])
     ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "combine"])
-    ap.add_argument("--mode", default="decode", choices=["decode", "append", "paged", "fp8"],
+    ap.add_argument("--mode", default="decode", choices=["decode", "append", "paged", "fp8", "int8"],
                     help="decode: gqa_decode; append: gqa_decode_append (the sq new tokens' K/V "
                          "stored and attended in one pass); paged: gqa_decode_paged over a "
                          "randomly ordered page pool; fp8: gqa_decode_fp8 over E4M3 codes with "
@@ -377,6 +378,20 @@ def main(argv=None):
         def call():
             gqa.decode_fp8(x["q"], kq, vq, ks, vs, x["seq_lens"], None, out,
                            workgroups=args.workgroups, merge=merge, stream=stream)
+    elif args.mode == "int8":
+        def quant8(t):
+            amax = t.float().abs().amax(dim=(0, 2, 3)).clamp_min(1e-6)
+            sc = (amax / 127.0).float().contiguous()
+            return torch.round(t.float() / sc.view(1, -1, 1, 1)).clamp(-128, 127).to(torch.int8).contiguous(), sc
+        kq, ks = quant8(x["k"])
+        vq, vs = quant8(x["v"])
+        plan = gqa.plan(gqa.shape_of(x["q"], kq), path=path, workgroups=args.workgroups, merge=merge)
+        log("[bench] int8 plan %s" % plan)
+        ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype) - sum_len * w.G * w.D * 2 + 2 * w.G * 4
+
+        def call():
+            gqa.decode_int8(x["q"], kq, vq, ks, vs, x["seq_lens"], None, out,
+                            workgroups=args.workgroups, merge=merge, stream=stream)
     else:
         def call():
             gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], None, out, path=path,
@@ -470,7 +485,8 @@ def main(argv=None):
             "workload": w.name, "B": w.B, "H": w.H, "G": w.G, "D": w.D, "T": w.T,
             "sq": w.sq, "seq_lens": ("uniform [%d, %d], seed %d" % (w.ragged[0], w.ragged[1], w.seed)
                                      if w.ragged else "all T"),
-            "sum_seq_lens": sum_len, "kv_dtype": w.dtype, "out_dtype": "f32",
+            "sum_seq_lens": sum_len, "kv_dtype": {"fp8": "fp8_e4m3", "int8": "int8"}.get(args.mode, w.dtype),
+            "out_dtype": "f32",
             "cache": "no sweep (warm)" if args.no_flush else "%d MiB read sweep before each step" % args.flush_mib,
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
             "workgroups": plan["workgroups"],
@@ -531,7 +547,7 @@ def main(argv=None):
         # the CPU-baseline leg: the only part of this script that runs the oracle
         log("[bench] timing the float64 oracle on the host (~%.0f s)" % args.cpu_seconds)
         del flush
-        extra = (kq, vq, ks, vs) if args.mode == "fp8" else (kn, vn) if args.mode == "append" else None
+        extra = (kq, vq, ks, vs) if args.mode in ("fp8", "int8") else (kn, vn) if args.mode == "append" else None
         try:
             result["max_abs_err_vs_oracle_b0"] = parity_spot_check(args, w, x, out, extra)
         except Exception as e:  # noqa: BLE001

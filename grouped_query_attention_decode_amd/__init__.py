@@ -26,7 +26,7 @@ import math
 import os
 import threading
 
-__all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "plan", "workspace_bytes",
+__all__ = ["decode", "decode_append", "decode_paged", "decode_fp8", "decode_int8", "plan", "workspace_bytes",
            "paged_workspace_bytes", "append_workspace_bytes", "decode_noalloc", "workspace_clear",
            "version", "library_path",
            "load_library", "GqaError", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_QK",
@@ -37,14 +37,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_ALLOC, GQA_ERR_HIP = range(5)
-GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_F16 = 0, 1, 2, 3
+GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_F16, GQA_INT8 = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_QK = 0, 1, 2, 3
 MERGE_AUTO, MERGE_IN_KERNEL, MERGE_COMBINE = 0, 1, 2
 
 # Every symbol include/gqa.h declares.
 EXPORTED_SYMBOLS = ("gqa_decode", "gqa_workspace_bytes", "gqa_append_workspace_bytes", "gqa_decode_ws",
                     "gqa_workspace_clear", "gqa_decode_noalloc",
-                    "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_append", "gqa_paged_workspace_bytes",
+                    "gqa_decode_ex", "gqa_decode_fp8", "gqa_decode_int8", "gqa_decode_append",
+                    "gqa_paged_workspace_bytes",
                     "gqa_decode_paged", "gqa_plan", "gqa_last_error", "gqa_version")
 
 
@@ -125,6 +126,8 @@ def load_library():
         lib.gqa_decode_fp8.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                        ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_fp8.restype = ctypes.c_int
+        lib.gqa_decode_int8.argtypes = lib.gqa_decode_fp8.argtypes
+        lib.gqa_decode_int8.restype = ctypes.c_int
         lib.gqa_decode_append.argtypes = [sp, vp, vp, vp, vp, vp, i32p, ctypes.c_float, vp, vp,
                                           ctypes.c_size_t, ctypes.POINTER(Options), vp]
         lib.gqa_decode_append.restype = ctypes.c_int
@@ -158,6 +161,8 @@ def _dtype_code(dt) -> int:
         return GQA_BF16
     if dt == torch.float16:
         return GQA_F16
+    if dt == torch.int8:
+        return GQA_INT8
     if dt in (torch.uint8, torch.float8_e4m3fn):
         return GQA_FP8_E4M3
     return 99  # rejected by the library as unsupported
@@ -417,6 +422,21 @@ def decode_fp8(q, k_codes, v_codes, k_scale=None, v_scale=None, seq_lens=None, s
     """Decode over an fp8 E4M3 cache: k_codes / v_codes [B,G,T,D] uint8 (or
     torch.float8_e4m3fn), k_scale / v_scale [G] float32 on the GPU or None
     (1.0); the value of code c in KV head g is e4m3(c) * scale[g]."""
+    return _decode_codes("gqa_decode_fp8", q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, out,
+                         workgroups, merge, workspace, stream)
+
+
+def decode_int8(q, k_codes, v_codes, k_scale=None, v_scale=None, seq_lens=None, scale=None, out=None,
+                *, workgroups=0, merge=0, workspace=None, stream=None):
+    """Decode over an int8 cache: k_codes / v_codes [B,G,T,D] torch.int8,
+    k_scale / v_scale [G] float32 on the GPU or None (1.0); the value of code
+    c in KV head g is c * scale[g]."""
+    return _decode_codes("gqa_decode_int8", q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, out,
+                         workgroups, merge, workspace, stream)
+
+
+def _decode_codes(entry, q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, out, workgroups, merge,
+                  workspace, stream):
     import torch
     lib = load_library()
     if q.dim() != 4 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape:
@@ -438,7 +458,7 @@ def decode_fp8(q, k_codes, v_codes, k_scale=None, v_scale=None, seq_lens=None, s
     ws_ptr, ws_len = _ws(workspace, dev)
     opts = _options(PATH_AUTO, workgroups, merge)
     with torch.cuda.device(dev):
-        st = lib.gqa_decode_fp8(
+        st = getattr(lib, entry)(
             ctypes.byref(shape), q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
             k_scale.data_ptr() if k_scale is not None else None,
             v_scale.data_ptr() if v_scale is not None else None,

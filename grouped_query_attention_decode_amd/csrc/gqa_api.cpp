@@ -69,13 +69,15 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         return fail(GQA_ERR_INVALID_ARG, "H (%d) must be a multiple of G (%d)", s->H, s->G);
     if (s->D != 64 && s->D != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", s->D);
     const bool f32 = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32 && s->out_dtype == GQA_F32;
-    const bool fp8 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_FP8_E4M3 && s->out_dtype == GQA_F32;
+    // an 8-bit cache: fp8 E4M3 or int8 codes (the planner treats both alike)
+    const bool i8 = s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_INT8 && s->out_dtype == GQA_F32;
+    const bool fp8 = (s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_FP8_E4M3 && s->out_dtype == GQA_F32) || i8;
     const bool bf16 = (s->q_dtype == GQA_BF16 && s->kv_dtype == GQA_BF16 && s->out_dtype == GQA_F32) || fp8;
     const bool f16 = s->q_dtype == GQA_F16 && s->kv_dtype == GQA_F16 && s->out_dtype == GQA_F32;
     if (!f32 && !bf16 && !f16)
         return fail(GQA_ERR_UNSUPPORTED,
                     "dtypes (q=%d, kv=%d, out=%d) not supported; use (F32,F32,F32), (BF16,BF16,F32), "
-                    "(F16,F16,F32) or (BF16,FP8_E4M3,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
+                    "(F16,F16,F32), (BF16,FP8_E4M3,F32) or (BF16,INT8,F32)", s->q_dtype, s->kv_dtype, s->out_dtype);
     if ((int64_t)s->T * s->D >= (int64_t)1 << 31)
         return fail(GQA_ERR_INVALID_ARG, "T * D must be below 2^31");
     if ((int64_t)s->B * s->H * s->sq * s->D >= (int64_t)1 << 40)
@@ -100,7 +102,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
     if (path_req == GQA_PATH_MFMA_QK && f16)
         return fail(GQA_ERR_UNSUPPORTED, "GQA_PATH_MFMA_QK reads bf16 only");
     if (fp8 && (path_req == GQA_PATH_VALU || path_req == GQA_PATH_MFMA_QK))
-        return fail(GQA_ERR_UNSUPPORTED, "an fp8 cache runs on GQA_PATH_MFMA only");
+        return fail(GQA_ERR_UNSUPPORTED, "an 8-bit cache runs on GQA_PATH_MFMA only");
 
     const int R = (int)R64;
     // bf16 and fp16 go to the matrix cores (both products unless asked otherwise);
@@ -114,6 +116,7 @@ gqa_status_t make_plan(const gqa_shape_t* s, const gqa_options_t* o, gqa::Plan* 
         p->path = gqa::Path::MFMA;
     p->kv_bf16 = bf16 && !fp8 ? 1 : 0;
     p->kv_fp8 = fp8 ? 1 : 0;
+    p->kv_i8 = i8 ? 1 : 0;
     p->kv_f16 = f16 ? 1 : 0;
     p->src = src;
     p->D = s->D;
@@ -355,7 +358,7 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
         return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 / fp16 matrix-core path");
     if ((srcx.k_scale || srcx.v_scale) && !plan.kv_fp8)
-        return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an fp8 cache only");
+        return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an 8-bit cache only");
     plan.src = srcx.src;
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale must be finite");
     if (shape->B == 0) return ok();
@@ -497,17 +500,35 @@ gqa_status_t gqa_decode_append(const gqa_shape_t* shape, const void* q, const vo
     return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
 }
 
+static gqa_status_t decode_codes(const gqa_shape_t* shape, const void* q, const void* k_cache, const void* v_cache,
+                                 const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                                 void* out, void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
+{
+    Source sx;
+    sx.k_scale = k_scale;
+    sx.v_scale = v_scale;
+    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
+    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
+}
+
 gqa_status_t gqa_decode_fp8(const gqa_shape_t* shape, const void* q, const void* k_cache, const void* v_cache,
                             const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
                             void* out, void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
 {
     if (shape && shape->kv_dtype != GQA_FP8_E4M3)
         return fail(GQA_ERR_INVALID_ARG, "gqa_decode_fp8 needs kv_dtype GQA_FP8_E4M3");
-    Source sx;
-    sx.k_scale = k_scale;
-    sx.v_scale = v_scale;
-    const bool lib_ws = workspace == nullptr && ws_bytes == 0;
-    return run(shape, q, k_cache, v_cache, seq_lens, scale, out, workspace, ws_bytes, lib_ws, opts, stream, sx);
+    return decode_codes(shape, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out, workspace, ws_bytes, opts,
+                        stream);
+}
+
+gqa_status_t gqa_decode_int8(const gqa_shape_t* shape, const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                             void* out, void* workspace, size_t ws_bytes, const gqa_options_t* opts, void* stream)
+{
+    if (shape && shape->kv_dtype != GQA_INT8)
+        return fail(GQA_ERR_INVALID_ARG, "gqa_decode_int8 needs kv_dtype GQA_INT8");
+    return decode_codes(shape, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out, workspace, ws_bytes, opts,
+                        stream);
 }
 
 // The contiguous shape a paged one plans as: T = page_size * max_pages.

@@ -52,7 +52,8 @@ __host__ __device__ constexpr int slot_floats(int rb, int d) { return rb * d + (
 struct Plan {
     Path path;
     int kv_bf16;        // 1: bf16 q/k/v, 0: fp32
-    int kv_fp8;         // 1: bf16 q, fp8 E4M3 k/v codes with per-KV-head scales
+    int kv_fp8;         // 1: bf16 q, 8-bit k/v codes (fp8 E4M3 or int8) with per-KV-head scales
+    int kv_i8;          // 1: the 8-bit codes are int8
     int kv_f16;         // 1: fp16 q/k/v
     int D;
     int R;              // (H/G)*sq query rows per KV head

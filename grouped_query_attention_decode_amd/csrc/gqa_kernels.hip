@@ -1411,6 +1411,30 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& c, uint4& lo, uint4&
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// 16 int8 codes -> two 8-element bf16 operands, each code c stored as the
+// unsigned u = c + 128 (exact: u has at most 8 significant bits, so its fp32
+// value truncates to bf16 without loss).  The offset of 128 is undone where
+// it lands: in the scores it adds the same amount to every score of a query
+// row (128 scale <q, 1>), which the softmax does not see; in the weighted V
+// sum it adds 128 to every output, subtracted when the rows are finished.
+__device__ __forceinline__ void i8x16_to_bf16(const uint4& c, uint4& lo, uint4& hi)
+{
+    const uint32_t w[4] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u, c.z ^ 0x80808080u, c.w ^ 0x80808080u};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t f0 = __float_as_uint((float)(w[i] & 0xFFu));
+        const uint32_t f1 = __float_as_uint((float)((w[i] >> 8) & 0xFFu));
+        const uint32_t f2 = __float_as_uint((float)((w[i] >> 16) & 0xFFu));
+        const uint32_t f3 = __float_as_uint((float)(w[i] >> 24));
+        // high halves of (f0, f1) and of (f2, f3): element 0 in the low half
+        o[2 * i] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        o[2 * i + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    }
+    lo = make_uint4(o[0], o[1], o[2], o[3]);
+    hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 constexpr int kPageWindow = 1024;        // block-table entries a wave keeps in LDS (paged cache)
 
 // Where the matrix-core pass reads K/V rows from.
@@ -1552,12 +1576,14 @@ __device__ __forceinline__ float sum_x32(float x)
 // next tiles' loads in flight; then written out, or left as a partial
 // (returned in *pd, stores issued, nothing waited for).  The NB 16-row
 // blocks share every K/V tile: it is read once for all of them.
-template <int D, int NB, int SRC, bool KV8, int NW = 1, class SM = MfaShared<D>, bool F16 = false>
+template <int D, int NB, int SRC, bool KV8, int NW = 1, class SM = MfaShared<D>, bool F16 = false,
+          bool I8 = false>
 __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb, const Piece& pc,
                                           const ChunkMap& cm, int chunk, Pending* pd)
 {
     static_assert(NW == 1 || (SRC == kSrcCache && !KV8), "row-split workgroups read a plain 16-bit cache");
-    static_assert(!F16 || !KV8, "an fp8 cache takes bf16 queries");
+    static_assert(!F16 || !KV8, "an 8-bit cache takes bf16 queries");
+    static_assert(!I8 || KV8, "int8 codes are an 8-bit cache");
     using MX = Mx<F16>;
     constexpr int NK = D / 32;           // k steps of the score product
     constexpr int NC = D / 16;           // column blocks of the V product
@@ -1705,12 +1731,20 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
 #pragma unroll
             for (int h = 0; h < NH; ++h)
 #pragma unroll
-                for (int s = 0; s < NLK; ++s) fp8x16_to_bf16(kin[h * NLK + s], kk[h][2 * s], kk[h][2 * s + 1]);
+                for (int s = 0; s < NLK; ++s) {
+                    if constexpr (I8)
+                        i8x16_to_bf16(kin[h * NLK + s], kk[h][2 * s], kk[h][2 * s + 1]);
+                    else
+                        fp8x16_to_bf16(kin[h * NLK + s], kk[h][2 * s], kk[h][2 * s + 1]);
+                }
 #pragma unroll
             for (int j = 0; j < NLV; ++j) {
                 const int c = lane + kWave * j;
                 uint4 lo, hi;
-                fp8x16_to_bf16(vv[j], lo, hi);
+                if constexpr (I8)
+                    i8x16_to_bf16(vv[j], lo, hi);
+                else
+                    fp8x16_to_bf16(vv[j], lo, hi);
                 uint16_t* dst = &vt[(c / CPR) * SE + (c % CPR) * 16];
                 *reinterpret_cast<uint4*>(dst) = lo;
                 *reinterpret_cast<uint4*>(dst + 8) = hi;
@@ -1909,12 +1943,15 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
     }
 
     // ---- end of the piece ------------------------------------------------------
-    float inv[NB], lse[NB];
+    // int8 codes: the weighted sum ran over c + 128, so 128 v_scale comes off
+    // every finished row (rows that see nothing stay 0)
+    float inv[NB], lse[NB], sub[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float l = sum_x32(sum_x16(l_run[nb]));
         inv[nb] = l > 0.0f ? out_scale / l : 0.0f;
         lse[nb] = l > 0.0f ? m_run[nb] + __log2f(l) : -INFINITY;
+        sub[nb] = (I8 && l > 0.0f) ? 128.0f * out_scale : 0.0f;
     }
     const int c_first = cm.of(pc.off);
     const int npieces = cm.of(pc.off + pc.L - 1) - c_first + 1;
@@ -1924,7 +1961,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
             if (!live[nb]) continue;
             float* o = a.out + (qrow0 + 16 * nb + col) * D + 4 * kg;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[nb][c] * inv[nb];
+            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4_t*>(o + 16 * c) = acc[nb][c] * inv[nb] - sub[nb];
         }
         return false;
     }
@@ -1937,7 +1974,7 @@ __device__ __forceinline__ bool mfa_piece(const Args& a, SM& sm, int R, int n_rb
         const int r = 16 * nb + col;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const f32x4_t o = acc[nb][c] * inv[nb];
+            const f32x4_t o = acc[nb][c] * inv[nb] - sub[nb];
             const float ov[4] = {o[0], o[1], o[2], o[3]};
             store4_coherent(part, mine + r * D + 16 * c + 4 * kg, ov);
         }
@@ -2052,7 +2089,7 @@ __device__ __forceinline__ void arrive_and_merge_mfa(const Args& a, const Pendin
     if (lane == 0) __hip_atomic_store(&a.counters[pd.seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NB, int SRC, bool KV8, bool F16 = false>
+template <int D, int NB, int SRC, bool KV8, bool F16 = false, bool I8 = false>
 __global__ void __launch_bounds__(kWave)
 decode_mfa(const int32_t* __restrict__ lens_in, const int nB, const int nT, const Args a, const int R, const int n_rb)
 {
@@ -2078,7 +2115,8 @@ decode_mfa(const int32_t* __restrict__ lens_in, const int nB, const int nT, cons
     Piece pc;
     while (it.next(a, sm.lens, pc)) {
         Pending pd;
-        if (mfa_piece<D, NB, SRC, KV8, 1, MfaShared<D>, F16>(a, sm, R, n_rb, pc, cm, chunk, &pd) && !a.deferred) {
+        if (mfa_piece<D, NB, SRC, KV8, 1, MfaShared<D>, F16, I8>(a, sm, R, n_rb, pc, cm, chunk, &pd) &&
+            !a.deferred) {
             partials_stored_before_arrival();    // own partial stores complete at device scope
             arrive_and_merge_mfa<D, 16 * NB>(a, pd, lane, R, cm);
         }
@@ -3068,13 +3106,13 @@ static DecodeFn pick_mqk(int rb)
     }
 }
 
-template <int SRC, bool KV8, bool F16 = false>
+template <int SRC, bool KV8, bool F16 = false, bool I8 = false>
 static DecodeFn pick_mfa(const Plan& p)
 {
     switch (p.row_block) {
-    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC, KV8, F16> : decode_mfa<128, 1, SRC, KV8, F16>;
-    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC, KV8, F16> : decode_mfa<128, 2, SRC, KV8, F16>;
-    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC, KV8, F16> : decode_mfa<128, 4, SRC, KV8, F16>;
+    case 16: return p.D == 64 ? decode_mfa<64, 1, SRC, KV8, F16, I8> : decode_mfa<128, 1, SRC, KV8, F16, I8>;
+    case 32: return p.D == 64 ? decode_mfa<64, 2, SRC, KV8, F16, I8> : decode_mfa<128, 2, SRC, KV8, F16, I8>;
+    case 64: return p.D == 64 ? decode_mfa<64, 4, SRC, KV8, F16, I8> : decode_mfa<128, 4, SRC, KV8, F16, I8>;
     default: return nullptr;
     }
 }
@@ -3122,7 +3160,10 @@ static DecodeFn pick(const Plan& p)
         return nullptr;
     }
     if (p.path == Path::MFMA) {
-        if (p.kv_fp8) return p.src == kSrcCache ? pick_mfa<kSrcCache, true>(p) : nullptr;
+        if (p.kv_fp8) {
+            if (p.src != kSrcCache) return nullptr;
+            return p.kv_i8 ? pick_mfa<kSrcCache, true, false, true>(p) : pick_mfa<kSrcCache, true>(p);
+        }
         if (p.kv_f16) {
             switch (p.src) {
             case kSrcCache: return pick_mfa<kSrcCache, false, true>(p);

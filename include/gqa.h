@@ -40,10 +40,10 @@
  *   - seq_lens values outside [0, T] are clamped on the device.
  *
  * Supported in this version: D in {64, 128}; dtypes (q, kv, out) =
- * (F32, F32, F32), (BF16, BF16, F32), (F16, F16, F32) or
- * (BF16, FP8_E4M3, F32) (the fp8 cache through gqa_decode_fp8, or
- * gqa_decode with unit scales; appended tokens and paged caches bf16 or
- * fp16);
+ * (F32, F32, F32), (BF16, BF16, F32), (F16, F16, F32),
+ * (BF16, FP8_E4M3, F32) or (BF16, INT8, F32) (the 8-bit caches through
+ * gqa_decode_fp8 / gqa_decode_int8, or gqa_decode with unit scales;
+ * appended tokens and paged caches bf16 or fp16);
  * H % G == 0;
  * any B >= 0, sq >= 1, T >= 1 with T * D < 2^31, B * H * sq * D < 2^40,
  * (H/G) * sq <= 2^20 and B * G * (row blocks per KV head) <= 2^18, where a
@@ -75,8 +75,9 @@ typedef enum {
  * [1, 8, 4096, 64] in the repeat_kv example of "Same GQA, Different
  * Execution Cost Across Backends", section 2, holds 2-byte values of a type
  * the page does not name); both products on the matrix cores in fp16 with
- * fp32 accumulation, the softmax weights as an fp16 pair hi + lo. */
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2, GQA_F16 = 3 } gqa_dtype_t;
+ * fp32 accumulation, the softmax weights as an fp16 pair hi + lo.
+ * GQA_INT8: two's-complement 8-bit integer codes, a cache only. */
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2, GQA_F16 = 3, GQA_INT8 = 4 } gqa_dtype_t;
 
 /* Problem shape.  H: query heads, G: KV heads ("num_key_value_heads"),
  * sq: new query tokens per sequence, T: cache capacity in rows, D: head dim. */
@@ -260,6 +261,25 @@ gqa_status_t gqa_decode_fp8(const gqa_shape_t *shape, const void *q,
                             const int32_t *seq_lens, float scale, void *out,
                             void *workspace, size_t ws_bytes,
                             const gqa_options_t *opts, void *stream);
+
+/*
+ * gqa_decode_int8 -- gqa_decode_fp8 with an int8 cache: shape->kv_dtype ==
+ * GQA_INT8, the cache value of a code c (-128 .. 127) in KV head g is
+ * c * scale[g] (k_scale / v_scale as for gqa_decode_fp8).  KV-cache
+ * quantization composes with GQA ("GQA (Grouped-Query Attention) 분석",
+ * section "장단점"); int8 with one scale per KV head is the other common
+ * 8-bit format.  Codes are converted to bf16 exactly (as c + 128, the offset
+ * removed from the scores by the softmax and from the outputs at the end);
+ * accumulation is fp32.  GQA_PATH_MFMA only.  gqa_decode and gqa_decode_ex
+ * also take an int8 shape, with unit scales.
+ * workspace NULL with ws_bytes 0: the library-owned workspace.
+ */
+gqa_status_t gqa_decode_int8(const gqa_shape_t *shape, const void *q,
+                             const void *k_cache, const void *v_cache,
+                             const float *k_scale, const float *v_scale,
+                             const int32_t *seq_lens, float scale, void *out,
+                             void *workspace, size_t ws_bytes,
+                             const gqa_options_t *opts, void *stream);
 
 /* Shape of a paged cache: page pools k_pages / v_pages [num_pages, G,
  * page_size, D]; block_table [B, max_pages] int32 (device) lists each

@@ -272,3 +272,25 @@ def decode_fp8_f64(q, k_codes, v_codes, k_scale, v_scale, seq_lens=None, scale=N
     the float64 oracle."""
     return decode_f64(q, dequant_fp8(k_codes, k_scale), dequant_fp8(v_codes, v_scale), seq_lens,
                       scale, threads=threads)
+
+
+def dequant_int8(codes, scale) -> np.ndarray:
+    """codes [B, G, T, D] (int8, two's complement), scale [G] -> float64
+    cache values code * scale[g] (an int8 cache with one scale per KV head;
+    the pages name KV quantization as composable with GQA -- "GQA
+    (Grouped-Query Attention) 분석", section "장단점" -- without a format)."""
+    c = np.asarray(codes.cpu().numpy() if hasattr(codes, "cpu") else codes)
+    if c.dtype != np.int8:
+        raise ValueError("int8 codes expected")
+    sc = _f64(scale)
+    if c.ndim != 4 or sc.shape != (c.shape[1],):
+        raise ValueError("expected codes [B,G,T,D] and scale [G]")
+    return c.astype(np.float64) * sc[None, :, None, None]
+
+
+def decode_int8_f64(q, k_codes, v_codes, k_scale, v_scale, seq_lens=None, scale=None,
+                    threads: int = 1):
+    """Decode over an int8 cache: dequantize every code (dequant_int8), then
+    the float64 oracle."""
+    return decode_f64(q, dequant_int8(k_codes, k_scale), dequant_int8(v_codes, v_scale), seq_lens,
+                      scale, threads=threads)

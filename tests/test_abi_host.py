@@ -370,6 +370,35 @@ def test_plan_fp16(lib):
     assert a > 0 and a == gqa.paged_workspace_bytes(gqa.PagedShape(q_dtype=gqa.GQA_BF16, kv_dtype=gqa.GQA_BF16, **ps))
 
 
+def test_plan_int8(lib):
+    """An int8 cache plans exactly as an fp8 one (one byte per element, the
+    one-block matrix-core kernel, four one-wave workgroups per CU); it runs
+    on GQA_PATH_MFMA only, with bf16 queries and fp32 out."""
+    for kw in (dict(B=32), dict(B=1, D=64), dict(B=64, G=1, T=8192), dict(B=8, sq=64)):
+        a = gqa.plan(_shape(kv_dtype=gqa.GQA_INT8, **kw))
+        assert a == gqa.plan(_shape(kv_dtype=gqa.GQA_FP8_E4M3, **kw)), kw
+    for kw, status in ((dict(path=gqa.PATH_VALU), gqa.GQA_ERR_UNSUPPORTED),
+                       (dict(path=gqa.PATH_MFMA_QK), gqa.GQA_ERR_UNSUPPORTED)):
+        with pytest.raises(gqa.GqaError) as ei:
+            gqa.plan(_shape(kv_dtype=gqa.GQA_INT8), **kw)
+        assert ei.value.status == status
+    for q_dt, out_dt in ((gqa.GQA_F16, gqa.GQA_F32), (gqa.GQA_F32, gqa.GQA_F32), (gqa.GQA_BF16, gqa.GQA_BF16)):
+        with pytest.raises(gqa.GqaError) as ei:
+            gqa.plan(_shape(q_dtype=q_dt, kv_dtype=gqa.GQA_INT8, out_dtype=out_dt))
+        assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+        assert "BF16,INT8,F32" in lib.gqa_last_error().decode()
+    # the entry points check the cache type before any device call
+    s = _shape(kv_dtype=gqa.GQA_FP8_E4M3)
+    st = lib.gqa_decode_int8(ctypes.byref(s), 16, 16, 16, None, None, None, ctypes.c_float(0.1), 16, None,
+                             ctypes.c_size_t(0), None, None)
+    assert st == gqa.GQA_ERR_INVALID_ARG and "GQA_INT8" in lib.gqa_last_error().decode()
+    s = _shape(kv_dtype=gqa.GQA_INT8)
+    st = lib.gqa_decode_fp8(ctypes.byref(s), 16, 16, 16, None, None, None, ctypes.c_float(0.1), 16, None,
+                            ctypes.c_size_t(0), None, None)
+    assert st == gqa.GQA_ERR_INVALID_ARG and "GQA_FP8_E4M3" in lib.gqa_last_error().decode()
+    assert gqa.workspace_bytes(_shape(kv_dtype=gqa.GQA_INT8)) == gqa.workspace_bytes(_shape(kv_dtype=gqa.GQA_FP8_E4M3))
+
+
 def test_append_workspace_bytes(lib):
     """Appended tokens above 16 query rows per KV head run one-wave
     workgroups of up to 64 rows, not the plain decode's 32 x 32 kernel:

@@ -1,7 +1,7 @@
 """Seeded random shapes through every entry point of the C ABI against the
-float64 oracle: gqa_decode, gqa_decode_append, gqa_decode_paged and
-gqa_decode_fp8, with random group sizes, head dims, context lengths (ragged,
-with empty and single-row sequences), new-token counts, page sizes, grid
+float64 oracle: gqa_decode, gqa_decode_append, gqa_decode_paged,
+gqa_decode_fp8 and gqa_decode_int8, with random group sizes, head dims,
+context lengths (ragged, with empty and single-row sequences), new-token counts, page sizes, grid
 sizes and merge modes -- so that tile ends, row windows, page windows and
 split points fall at arbitrary rows; the fp16 entry points on the same
 shapes.  Tolerance as for the fixed cases (bf16 inputs, fp32 accumulation:
@@ -172,5 +172,22 @@ def test_random_fp8(gqa, orc, i):
     want = orc.decode_fp8_f64(x["q"], kc, vc, ks, vs, x["seq_lens"], threads=8)
     got = gqa.decode_fp8(x["q"].cuda(), kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda(), x["seq_lens"].cuda(),
                          workgroups=c["P"], merge=c["merge"])
+    torch.cuda.synchronize()
+    assert _err(got, want) <= TOL["bf16"], c
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_int8(gqa, orc, i):
+    c = _shape(i)
+    B, G, D, T = c["B"], c["G"], c["D"], c["T"]
+    x = gi.make_custom(B, c["H"], G, D, T, c["sq"], dtype="bf16", seed=c["seed"], seq_lens=c["lens"])
+    gen = torch.Generator().manual_seed(c["seed"] + 4)
+    kc = torch.randint(-128, 128, (B, G, T, D), generator=gen, dtype=torch.int8)
+    vc = torch.randint(-128, 128, (B, G, T, D), generator=gen, dtype=torch.int8)
+    ks = (torch.rand(G, generator=gen) * 0.01 + 0.001).float()
+    vs = (torch.rand(G, generator=gen) * 0.01 + 0.001).float()
+    want = orc.decode_int8_f64(x["q"], kc, vc, ks, vs, x["seq_lens"], threads=8)
+    got = gqa.decode_int8(x["q"].cuda(), kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda(), x["seq_lens"].cuda(),
+                          workgroups=c["P"], merge=c["merge"])
     torch.cuda.synchronize()
     assert _err(got, want) <= TOL["bf16"], c

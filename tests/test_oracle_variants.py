@@ -167,3 +167,36 @@ def test_fp8_decode_equals_decode_of_dequantized_cache(oracle_mod):
     got3 = oracle_mod.decode_fp8_f64(q, kc, vc, 2 * ks, vs, lens, scale=0.5 / math.sqrt(D))
     assert np.allclose(got3, oracle_mod.decode_fp8_f64(q, kc, vc, ks, vs, lens, scale=1 / math.sqrt(D)),
                        rtol=0, atol=1e-12)
+
+
+def test_int8_dequant_literal_codes(oracle_mod):
+    """Two's-complement codes times the KV head's scale, at the ends of the
+    range (0x80 = -128, 0x7F = 127) and around zero."""
+    codes = np.array([0, 1, -1, 127, -128, 64, -64, 5], dtype=np.int8).reshape(1, 2, 1, 4)
+    sc = np.array([0.5, 2.0 ** -7])
+    got = oracle_mod.dequant_int8(codes, sc)
+    want = np.array([[0.0, 0.5, -0.5, 63.5], [-1.0, 0.5, -0.5, 5.0 / 128]]).reshape(1, 2, 1, 4)
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        oracle_mod.dequant_int8(codes.astype(np.uint8), sc)
+
+
+def test_int8_decode_equals_decode_of_dequantized_cache(oracle_mod):
+    """Every int8 code times a power-of-two scale is exactly a bf16 number
+    (at most 8 significant bits), so the int8 decode equals the bf16 decode
+    of that cache; V's scale scales the output."""
+    B, H, G, D, T, sq = 2, 8, 2, 32, 50, 2
+    gen = torch.Generator().manual_seed(71)
+    kc = torch.randint(-128, 128, (B, G, T, D), generator=gen, dtype=torch.int8)
+    vc = torch.randint(-128, 128, (B, G, T, D), generator=gen, dtype=torch.int8)
+    ks = torch.tensor([2.0 ** -5, 2.0 ** -9])
+    vs = torch.tensor([1.0, 0.25])
+    q = torch.randn(B, H, sq, D, generator=gen).to(torch.bfloat16)
+    lens = [50, 9]
+    kd = kc.to(torch.float32) * ks.view(1, G, 1, 1)
+    vd = vc.to(torch.float32) * vs.view(1, G, 1, 1)
+    assert torch.equal(kd.to(torch.bfloat16).to(torch.float32), kd)      # exact in bf16
+    want = oracle_mod.decode_f64(q, kd.to(torch.bfloat16), vd.to(torch.bfloat16), lens)
+    got = oracle_mod.decode_int8_f64(q, kc, vc, ks, vs, lens)
+    assert np.array_equal(got, want)
+    assert np.array_equal(oracle_mod.decode_int8_f64(q, kc, vc, ks, 2 * vs, lens), 2 * got)
