@@ -390,7 +390,10 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens=None, scale=None, ou
                  path=PATH_AUTO, workgroups=0, merge=0, workspace=None, stream=None):
     """Decode attention over a paged cache: k_pages / v_pages
     [num_pages, G, page_size, D], block_table [B, max_pages] int32 (row t of
-    sequence b is row t % page_size of page block_table[b, t // page_size])."""
+    sequence b is row t % page_size of page block_table[b, t // page_size]).
+    Pages of bf16 or fp16, or of 8-bit codes (uint8 / float8_e4m3fn for E4M3,
+    int8) read with unit scales: fold one K scale into ``scale`` and multiply
+    the output by one V scale."""
     import torch
     lib = load_library()
     if q.dim() != 4 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:

@@ -355,8 +355,10 @@ gqa_status_t run(const gqa_shape_t* shape, const void* q, const void* k, const v
     gqa::Plan plan;
     gqa_status_t st = make_plan(shape, opts, &plan, srcx.src);
     if (st != GQA_OK) return st;
-    if (srcx.src != 0 && (plan.path != gqa::Path::MFMA || plan.kv_fp8))
-        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the bf16 / fp16 matrix-core path");
+    if (srcx.src != 0 && plan.path != gqa::Path::MFMA)
+        return fail(GQA_ERR_UNSUPPORTED, "appended tokens and paged caches need the matrix-core path");
+    if (srcx.src == 1 && plan.kv_fp8)
+        return fail(GQA_ERR_UNSUPPORTED, "appended tokens need a bf16 / fp16 cache");
     if ((srcx.k_scale || srcx.v_scale) && !plan.kv_fp8)
         return fail(GQA_ERR_INVALID_ARG, "k_scale / v_scale apply to an 8-bit cache only");
     plan.src = srcx.src;

@@ -3161,8 +3161,11 @@ static DecodeFn pick(const Plan& p)
     }
     if (p.path == Path::MFMA) {
         if (p.kv_fp8) {
-            if (p.src != kSrcCache) return nullptr;
-            return p.kv_i8 ? pick_mfa<kSrcCache, true, false, true>(p) : pick_mfa<kSrcCache, true>(p);
+            if (p.src == kSrcCache)
+                return p.kv_i8 ? pick_mfa<kSrcCache, true, false, true>(p) : pick_mfa<kSrcCache, true>(p);
+            if (p.src == kSrcPaged)
+                return p.kv_i8 ? pick_mfa<kSrcPaged, true, false, true>(p) : pick_mfa<kSrcPaged, true>(p);
+            return nullptr;
         }
         if (p.kv_f16) {
             switch (p.src) {

@@ -43,7 +43,7 @@
  * (F32, F32, F32), (BF16, BF16, F32), (F16, F16, F32),
  * (BF16, FP8_E4M3, F32) or (BF16, INT8, F32) (the 8-bit caches through
  * gqa_decode_fp8 / gqa_decode_int8, or gqa_decode with unit scales;
- * appended tokens and paged caches bf16 or fp16);
+ * appended tokens bf16 or fp16; paged caches also 8-bit, with unit scales);
  * H % G == 0;
  * any B >= 0, sq >= 1, T >= 1 with T * D < 2^31, B * H * sq * D < 2^40,
  * (H/G) * sq <= 2^20 and B * G * (row blocks per KV head) <= 2^18, where a
@@ -303,7 +303,9 @@ size_t gqa_paged_workspace_bytes(const gqa_paged_shape_t *shape);
  * "GQA (Grouped-Query Attention) 분석", section "장단점" and the checklist
  * of item 4 of "동작 원리").  Only the table entries for rows below L_b are
  * read; an entry outside [0, num_pages) is clamped into it (no fault, but
- * the result is then meaningless).  bf16 or fp16 (GQA_PATH_MFMA).
+ * the result is then meaningless).  bf16 or fp16, or 8-bit codes (fp8
+ * E4M3 or int8) read with unit scales: fold a K scale into `scale` and
+ * multiply the output by a V scale (GQA_PATH_MFMA).
  * workspace NULL with ws_bytes 0: the library-owned workspace.
  */
 gqa_status_t gqa_decode_paged(const gqa_paged_shape_t *shape, const void *q,

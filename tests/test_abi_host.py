@@ -430,3 +430,19 @@ def test_noalloc_refuses_oversized_workspace_before_any_gpu_work(lib):
     st = lib.gqa_decode_noalloc(ctypes.byref(s), 16, 16, 16, None, ctypes.c_float(0.1), 16, ctypes.byref(o), None)
     assert st == gqa.GQA_ERR_ALLOC
     assert "scratch" in lib.gqa_last_error().decode()
+
+
+def test_plan_paged_codes(lib):
+    """A page pool of 8-bit codes (fp8 E4M3 or int8) plans as the contiguous
+    8-bit cache of T = page_size * max_pages rows (the same kernel and grid:
+    paging moves rows only); appended tokens into an 8-bit cache are refused
+    before any device call."""
+    ps = dict(B=32, H=32, G=8, sq=1, D=128, page_size=16, num_pages=8192, max_pages=256, out_dtype=gqa.GQA_F32)
+    for kv in (gqa.GQA_FP8_E4M3, gqa.GQA_INT8):
+        a = gqa.paged_workspace_bytes(gqa.PagedShape(q_dtype=gqa.GQA_BF16, kv_dtype=kv, **ps))
+        assert a > 0 and a == gqa.plan(_shape(B=32, T=16 * 256, kv_dtype=kv))["workspace_bytes"]
+        assert gqa.paged_workspace_bytes(gqa.PagedShape(q_dtype=gqa.GQA_F16, kv_dtype=kv, **ps)) == 0
+        s = _shape(kv_dtype=kv)
+        st = lib.gqa_decode_append(ctypes.byref(s), 16, 16, 16, 16, 16, None, ctypes.c_float(0.1), 16, None,
+                                   ctypes.c_size_t(0), None, None)
+        assert st == gqa.GQA_ERR_UNSUPPORTED and "bf16 / fp16 cache" in lib.gqa_last_error().decode()
