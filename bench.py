@@ -253,11 +253,14 @@ def parity_spot_check(args, w, x, out, extra):
     b = 0
     xb = {k: v[b:b + 1].cpu() for k, v in x.items()}
     scale = 1.0 / math.sqrt(w.D)
-    if args.mode in ("fp8", "int8"):
+    codes = args.mode if args.mode in ("fp8", "int8") else args.page_codes if args.mode == "paged" else "none"
+    if codes != "none":
         kq, vq, ks, vs = extra
-        fn = oracle.decode_fp8_f64 if args.mode == "fp8" else oracle.decode_int8_f64
+        fn = oracle.decode_fp8_f64 if codes == "fp8" else oracle.decode_int8_f64
         want = fn(xb["q"], kq[b:b + 1].cpu(), vq[b:b + 1].cpu(), ks.cpu(), vs.cpu(), xb["seq_lens"], scale,
                   threads=8)
+        if args.mode == "paged":
+            out = out * vs[0].item()      # the V scale a caller applies to a pool read with unit scales
     elif args.mode == "append":
         kn, vn = extra
         # the cache already holds the appended rows (every step stores the same ones)
@@ -286,6 +289,10 @@ def main(argv=None):
                          "randomly ordered page pool; fp8: gqa_decode_fp8 over E4M3 codes with "
                          "per-KV-head scales (amax / 448)")
     ap.add_argument("--page-size", type=int, default=16)
+    ap.add_argument("--page-codes", default="none", choices=["none", "fp8", "int8"],
+                    help="paged mode: a pool of 8-bit codes read with unit scales -- E4M3 of the "
+                         "cache values, or int8 round(32 x value) with 1/32 folded into the score "
+                         "scale and applied to the output")
     ap.add_argument("--flush-mib", type=int, default=FLUSH_BYTES >> 20,
                     help="size of the read sweep before every step, in MiB (at least twice the "
                          "256 MB Infinity Cache)")
@@ -353,16 +360,29 @@ def main(argv=None):
         ps = args.page_size
         n = w.T // ps
         perm = torch.randperm(w.B * n, generator=torch.Generator().manual_seed(w.seed + 11))
-        kp = torch.empty(w.B * n, w.G, ps, w.D, dtype=x["k"].dtype, device=dev)
+        page_scale, pscore = 1.0, None
+        if args.page_codes == "fp8":
+            kc = x["k"].float().to(torch.float8_e4m3fn).view(torch.uint8)
+            vc = x["v"].float().to(torch.float8_e4m3fn).view(torch.uint8)
+        elif args.page_codes == "int8":
+            page_scale = 1.0 / 32
+            kc = torch.round(x["k"].float() * 32).clamp(-128, 127).to(torch.int8)
+            vc = torch.round(x["v"].float() * 32).clamp(-128, 127).to(torch.int8)
+        else:
+            kc, vc = x["k"], x["v"]
+        if args.page_codes != "none":
+            pscore = page_scale / math.sqrt(w.D)
+            ub -= sum_len * w.G * w.D * 2          # one byte per K/V element
+        kp = torch.empty(w.B * n, w.G, ps, w.D, dtype=kc.dtype, device=dev)
         vp = torch.empty_like(kp)
         idx = perm.view(w.B, n).to(dev)
-        kp[idx.reshape(-1)] = x["k"].view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
-        vp[idx.reshape(-1)] = x["v"].view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
+        kp[idx.reshape(-1)] = kc.view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
+        vp[idx.reshape(-1)] = vc.view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
         bt = idx.to(torch.int32).contiguous()
         ub += int(sum((int(L) + ps - 1) // ps for L in x["seq_lens"].clamp(0, w.T).tolist())) * 4
 
         def call():
-            gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], None, out, path=path,
+            gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], pscore, out, path=path,
                              workgroups=args.workgroups, merge=merge, stream=stream)
     elif args.mode == "fp8":
         def quant(t):
@@ -467,7 +487,8 @@ def main(argv=None):
     gbs = ub / (ms * 1e-3) / 1e9
     achieved = gbs      # one kernel per step: the step is the kernel
     sha = kernel_source_sha()
-    traffic = load_traffic(w.name if args.mode == "decode" else "%s_%s" % (w.name, args.mode), sha)
+    mode_key = args.mode + ("_" + args.page_codes if args.mode == "paged" and args.page_codes != "none" else "")
+    traffic = load_traffic(w.name if args.mode == "decode" else "%s_%s" % (w.name, mode_key), sha)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -485,7 +506,9 @@ def main(argv=None):
             "workload": w.name, "B": w.B, "H": w.H, "G": w.G, "D": w.D, "T": w.T,
             "sq": w.sq, "seq_lens": ("uniform [%d, %d], seed %d" % (w.ragged[0], w.ragged[1], w.seed)
                                      if w.ragged else "all T"),
-            "sum_seq_lens": sum_len, "kv_dtype": {"fp8": "fp8_e4m3", "int8": "int8"}.get(args.mode, w.dtype),
+            "sum_seq_lens": sum_len,
+            "kv_dtype": {"fp8": "fp8_e4m3", "int8": "int8"}.get(
+                args.page_codes if args.mode == "paged" else args.mode, w.dtype),
             "out_dtype": "f32",
             "cache": "no sweep (warm)" if args.no_flush else "%d MiB read sweep before each step" % args.flush_mib,
             "path": {1: "valu", 2: "mfma", 3: "mfma_qk"}.get(plan["path"], "?"),
@@ -493,6 +516,7 @@ def main(argv=None):
             "waves_per_group": plan["waves_per_group"],
             "combine_kernel": bool(plan["combine"]),
             "mode": args.mode,
+            **({"page_size": args.page_size, "page_codes": args.page_codes} if args.mode == "paged" else {}),
         },
         "us_per_step": round(ms * 1e3, 2),
         "timing": "device time per step: K steps back to back after cache sweeps, minus as many sweeps alone, in %d alternating blocks" % nblk,
@@ -548,6 +572,9 @@ def main(argv=None):
         log("[bench] timing the float64 oracle on the host (~%.0f s)" % args.cpu_seconds)
         del flush
         extra = (kq, vq, ks, vs) if args.mode in ("fp8", "int8") else (kn, vn) if args.mode == "append" else None
+        if args.mode == "paged" and args.page_codes != "none":
+            one = torch.full((w.G,), page_scale)
+            extra = (kc, vc, one, one)
         try:
             result["max_abs_err_vs_oracle_b0"] = parity_spot_check(args, w, x, out, extra)
         except Exception as e:  # noqa: BLE001
