@@ -141,3 +141,20 @@ def test_paged_codes_refusals(gqa):
     with pytest.raises(gqa.GqaError) as ei:
         gqa.decode_append(q, kn, kn.clone(), kc, kc.clone())
     assert ei.value.status == gqa.GQA_ERR_UNSUPPORTED
+
+
+def test_paged_fp8_pool_as_float8_dtype(gqa):
+    """A pool passed as torch.float8_e4m3fn is the same bytes as its uint8
+    view: the same call, the same bits."""
+    B, H, G, D, T, ps = 2, 16, 4, 128, 256, 32
+    x = gi.make_custom(B, H, G, D, T, 1, dtype="bf16", seed=774, seq_lens=[256, 90])
+    kc, _ = _codes(x["k"], "fp8")
+    vc, _ = _codes(x["v"], "fp8")
+    perm = np.random.default_rng(775).permutation(B * (T // ps))
+    kp, bt = _to_pages(kc, ps, perm)
+    vp, _ = _to_pages(vc, ps, perm)
+    q, sl, kp, vp, bt = x["q"].cuda(), x["seq_lens"].cuda(), kp.cuda(), vp.cuda(), bt.cuda()
+    a = gqa.decode_paged(q, kp, vp, bt, sl)
+    b = gqa.decode_paged(q, kp.view(torch.float8_e4m3fn), vp.view(torch.float8_e4m3fn), bt, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
