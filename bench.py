@@ -81,6 +81,19 @@ def useful_bytes(B, H, G, D, sq, sum_len, dtype: str) -> int:
     return kv_bytes(G, D, sum_len, dtype) + q_bytes(B, H, D, sq, dtype) + o_bytes(B, H, D, sq)
 
 
+def code_cache_bytes(B, H, G, D, sq, sum_len, scales: bool) -> int:
+    """useful_bytes for an 8-bit cache (fp8 E4M3 or int8 codes, one byte per
+    K/V element) with bf16 queries: plus the two [G] fp32 scale arrays when
+    the call reads them (not for a pool read with unit scales)."""
+    return 2 * sum_len * G * D + q_bytes(B, H, D, sq, "bf16") + o_bytes(B, H, D, sq) + (2 * G * 4 if scales else 0)
+
+
+def page_table_bytes(seq_lens, T: int, page_size: int) -> int:
+    """Block-table entries a paged call reads: one int32 per page that holds
+    a row below L_b (L_b clamped to [0, T])."""
+    return 4 * sum((min(max(int(L), 0), T) + page_size - 1) // page_size for L in seq_lens)
+
+
 def flops(H, D, sq, sum_len) -> int:
     """2 FLOP per multiply-add; scores and weighted sum each H*sq*L*D MACs
     ("질의 헤드는 그대로, 키·값 헤드만 줄인다", section on what shrinks: the
@@ -372,14 +385,14 @@ def main(argv=None):
             kc, vc = x["k"], x["v"]
         if args.page_codes != "none":
             pscore = page_scale / math.sqrt(w.D)
-            ub -= sum_len * w.G * w.D * 2          # one byte per K/V element
+            ub = code_cache_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, scales=False)
         kp = torch.empty(w.B * n, w.G, ps, w.D, dtype=kc.dtype, device=dev)
         vp = torch.empty_like(kp)
         idx = perm.view(w.B, n).to(dev)
         kp[idx.reshape(-1)] = kc.view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
         vp[idx.reshape(-1)] = vc.view(w.B, w.G, n, ps, w.D).transpose(1, 2).reshape(w.B * n, w.G, ps, w.D)
         bt = idx.to(torch.int32).contiguous()
-        ub += int(sum((int(L) + ps - 1) // ps for L in x["seq_lens"].clamp(0, w.T).tolist())) * 4
+        ub += page_table_bytes(x["seq_lens"].tolist(), w.T, ps)
 
         def call():
             gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], pscore, out, path=path,
@@ -393,7 +406,7 @@ def main(argv=None):
         vq, vs = quant(x["v"])
         plan = gqa.plan(gqa.shape_of(x["q"], kq), path=path, workgroups=args.workgroups, merge=merge)
         log("[bench] fp8 plan %s" % plan)
-        ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype) - sum_len * w.G * w.D * 2 + 2 * w.G * 4
+        ub = code_cache_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, scales=True)
 
         def call():
             gqa.decode_fp8(x["q"], kq, vq, ks, vs, x["seq_lens"], None, out,
@@ -407,7 +420,7 @@ def main(argv=None):
         vq, vs = quant8(x["v"])
         plan = gqa.plan(gqa.shape_of(x["q"], kq), path=path, workgroups=args.workgroups, merge=merge)
         log("[bench] int8 plan %s" % plan)
-        ub = useful_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, w.dtype) - sum_len * w.G * w.D * 2 + 2 * w.G * 4
+        ub = code_cache_bytes(w.B, w.H, w.G, w.D, w.sq, sum_len, scales=True)
 
         def call():
             gqa.decode_int8(x["q"], kq, vq, ks, vs, x["seq_lens"], None, out,

@@ -3,6 +3,7 @@ reports, pinned to the sizes the pages print (tests/golden/sizes.txt) and
 to a brute-force count of the multiplies.  CPU only."""
 import os
 
+import numpy as np
 import pytest
 
 import bench
@@ -85,3 +86,24 @@ def test_headline_bytes_recomputed_by_hand():
     # batched GQA-8 decode with the seed's sum of lengths 80,681:
     # 2 * 80681 * 8 * 128 * 2 + 32*32*128*2 + 32*32*128*4
     assert bench.useful_bytes(32, 32, 8, 128, 1, 80681, "bf16") == 331255808
+
+
+def test_code_cache_bytes_recomputed_by_hand():
+    # the headline workload with an 8-bit cache: 2 * 80681 * 8 * 128 * 1 codes
+    # + 32*32*128*2 (bf16 q) + 32*32*128*4 (fp32 out) + 2 * 8 * 4 (scales)
+    assert bench.code_cache_bytes(32, 32, 8, 128, 1, 80681, scales=True) == 166021184
+    assert bench.code_cache_bytes(32, 32, 8, 128, 1, 80681, scales=False) == 166021120
+    # one byte less per K/V element than the bf16 cache, nothing else changes
+    assert (bench.useful_bytes(32, 32, 8, 128, 1, 80681, "bf16")
+            - bench.code_cache_bytes(32, 32, 8, 128, 1, 80681, scales=False)) == 2 * 80681 * 8 * 128
+
+
+@pytest.mark.parametrize("ps", [16, 64, 256])
+def test_page_table_bytes_count_the_pages_rows_touch(ps):
+    """One int32 per page holding a row below L (clamped to [0, T]), counted
+    here by walking every row."""
+    rng = np.random.default_rng(ps)
+    T = 4096
+    lens = [0, 1, ps - 1, ps, ps + 1, T, T + 500, -3] + rng.integers(0, T + 1, 20).tolist()
+    walked = sum(len({t // ps for t in range(min(max(L, 0), T))}) for L in lens)
+    assert bench.page_table_bytes(lens, T, ps) == 4 * walked
