@@ -158,3 +158,38 @@ def test_paged_fp8_pool_as_float8_dtype(gqa):
     b = gqa.decode_paged(q, kp.view(torch.float8_e4m3fn), vp.view(torch.float8_e4m3fn), bt, sl)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+def test_paged_codes_full_size_sampled(gqa, orc, kind):
+    """The batched GQA-8 workload (B = 32, H = 32, G = 8, D = 128, ragged
+    T <= 4096) as a randomly ordered pool of 16-row pages, in the launch the
+    benchmark times: the whole batch on the GPU, sampled sequences against
+    the oracle on the host, and the whole output against the contiguous
+    8-bit call bit for bit."""
+    w = gi.WORKLOADS[gi.HEADLINE]
+    x = gi.make_inputs(w, device="cuda")
+    B, G, T, D, ps = w.B, w.G, w.T, w.D, 16
+    kc, ks = _codes(x["k"], kind)
+    vc, vs = _codes(x["v"], kind)
+    n = T // ps
+    perm = torch.randperm(B * n, generator=torch.Generator().manual_seed(776)).cuda()
+    kp = torch.empty(B * n, G, ps, D, dtype=kc.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = kc.view(B, G, n, ps, D).transpose(1, 2).reshape(B * n, G, ps, D)
+    vp[perm] = vc.view(B, G, n, ps, D).transpose(1, 2).reshape(B * n, G, ps, D)
+    bt = perm.view(B, n).to(torch.int32).contiguous()
+    s = ks / math.sqrt(D)
+    got = gqa.decode_paged(x["q"], kp, vp, bt, x["seq_lens"], scale=s)
+    contiguous = gqa.decode_fp8 if kind == "fp8" else gqa.decode_int8
+    ref = contiguous(x["q"], kc, vc, None, None, x["seq_lens"], scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    fn = orc.decode_fp8_f64 if kind == "fp8" else orc.decode_int8_f64
+    one = torch.ones(G)
+    for b in (0, 17, 31):
+        want = fn(x["q"][b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(), one * ks, one * vs,
+                  x["seq_lens"][b:b + 1].cpu(), 1.0 / math.sqrt(D), threads=8)
+        assert _err(got[b:b + 1] * vs, want) <= TOL, (kind, b)
+    del x, kc, vc, kp, vp, got, ref
+    torch.cuda.empty_cache()
